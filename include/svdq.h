@@ -1,0 +1,163 @@
+/*
+ * svdq.h -- C ABI of libsvdq.so, the MI355X (gfx950) hot path of the SVDQuant
+ * 4-bit linear layer.
+ *
+ * The layer (SVDQuant notes page, hoonably.github.io/blog/svdquant, section 4.2,
+ * the low-rank decomposition identity; section 4.3, Nunchaku kernel fusion):
+ *
+ *     Y = act( deQ(Q4(X_hat)) . deQ(Q4(R))^T  +  (X_hat L1) L2  +  b ),
+ *     X_hat = X diag(lambda)^-1,
+ *
+ * with lambda the per-input-channel smoothing factor, L1 (K x r) and L2 (r x N)
+ * the 16-bit low-rank branch, R (N x K here, nn.Linear orientation) the residual
+ * quantized to 4 bits, b the bias and act the identity or GELU.  Q4 is the
+ * max-scaled quantizer of section 3 applied per group of g consecutive elements
+ * along K:
+ *   SVDQ_MXFP4    : E2M1 codes, one E8M0 (power of two) scale per 32;
+ *                   scale 2^e, e = floor(log2 amax) - 2 clamped to [-127, 127],
+ *                   codes = nearest E2M1 of x / 2^e, ties to even, saturating at 6.
+ *   SVDQ_INT4_G64 : two's complement codes, one fp16 scale per 64;
+ *                   s = fp16(fp32(amax / 7)) (clamped to 65504),
+ *                   q = clamp(rint(fp32(x / s)), -8, 7), 0 when s == 0.
+ * All float32 decision arithmetic is IEEE (correctly rounded divisions).
+ *
+ * Two launches per layer, as section 4.3 describes: svdq_quantize_act (smooth,
+ * group amax, scale, encode, pack, and the down projection X_hat L1 in the same
+ * pass over X) and svdq_gemm (the block-scaled 4-bit GEMM whose epilogue adds
+ * (X_hat L1) L2, the bias and the activation).  svdq_linear runs both.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device buffers are device pointers owned by the caller;
+ *     the library never allocates, frees or synchronizes the host.
+ *   - Every call enqueues its work on `stream` (a hipStream_t; NULL is the null
+ *     stream) and returns without waiting for it.
+ *   - Validation is synchronous and happens before any launch: on an error the
+ *     outputs are untouched and nothing is enqueued.  Checks, in this order:
+ *     NULL pointers, shapes, formats/flags, alignment, workspace size, then the
+ *     device (the current device must be gfx950; otherwise SVDQ_ERR_DEVICE, the
+ *     load-time capability check the Diffusers integration page describes).
+ *   - No C++ exception crosses the ABI.  Calls that overlap on one stream are
+ *     ordered; the library holds no mutable state (apart from a per-device
+ *     cache of the architecture check) and is re-entrant.
+ *
+ * Shapes: K % 512 == 0, 16 <= N, N % 16 == 0, 0 <= rank <= 256, M >= 0,
+ * K <= 65536, N <= 65536.  Row strides (ldx, ldy) are in elements and
+ * multiples of 8 (16-byte rows).  Device buffers must be 16-byte aligned;
+ * packed weights and activation workspaces 256-byte aligned.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = 1,      /* a required pointer is NULL                         */
+  SVDQ_ERR_SHAPE = 2,     /* K, N, rank, M, ldx or ldy outside the stated set    */
+  SVDQ_ERR_FORMAT = 3,    /* unknown format or epilogue flag                     */
+  SVDQ_ERR_ALIGN = 4,     /* a pointer or stride is not aligned as required      */
+  SVDQ_ERR_WORKSPACE = 5, /* workspace smaller than svdq_act_bytes               */
+  SVDQ_ERR_DEVICE = 6,    /* no device, or the current device is not gfx950      */
+  SVDQ_ERR_LAUNCH = 7     /* a kernel launch failed                              */
+} svdq_status;
+
+typedef enum {
+  SVDQ_MXFP4 = 1,         /* E2M1 codes, E8M0 scale per 32 along K   */
+  SVDQ_INT4_G64 = 2       /* int4 codes, fp16 scale per 64 along K   */
+} svdq_format;
+
+/* Epilogue flags of svdq_gemm / svdq_linear. */
+enum {
+  SVDQ_EPI_LOWRANK = 1u,  /* add (X_hat L1) L2 (ignored when rank == 0)          */
+  SVDQ_EPI_BIAS = 2u,     /* add b                                              */
+  SVDQ_EPI_GELU = 4u,     /* apply GELU, erf form y * Phi(y), last              */
+  SVDQ_EPI_OUT_F32 = 8u   /* Y is float32 (default: bf16, round to nearest even) */
+};
+
+/* One layer: format, input features K, output features N, low-rank rank. */
+typedef struct {
+  int32_t fmt;
+  int32_t K;
+  int32_t N;
+  int32_t rank;
+} svdq_layer_desc;
+
+/* Bytes of the packed weight blob for this layer; 0 if the descriptor is invalid.
+ * Host-only query, no device access. */
+size_t svdq_weight_bytes(const svdq_layer_desc* d);
+
+/* Bytes of the activation workspace for M rows (packed codes, scales and the
+ * down projection X_hat L1); 0 if the descriptor or M is invalid. Host-only. */
+size_t svdq_act_bytes(const svdq_layer_desc* d, int64_t M);
+
+/* Quantize and pack one layer's weights once (load time).
+ * Definition: section 4.2 of the SVDQuant notes page -- R is the residual
+ * diag(lambda) W - L1 L2 that is quantized to 4 bits; L1, L2 stay 16-bit.
+ *   R       device, float32, N x K row-major (row n = output channel n)
+ *   L1      device, bf16 bits, K x rank row-major (may be NULL iff rank == 0)
+ *   L2      device, bf16 bits, rank x N row-major (may be NULL iff rank == 0)
+ *   lambda  device, float32[K], smoothing factors (finite, > 0)
+ *   bias    device, bf16 bits [N], or NULL for a zero bias
+ *   w_packed device, svdq_weight_bytes(d) bytes, 256-byte aligned; opaque layout
+ * R's codes and scales are computed on the device with the Q4 rule above.
+ * Repacking with adapter factors concatenated onto L1/L2 (rank grows) leaves the
+ * 4-bit residual section byte-identical (SVDQuant abstract: adapters need no
+ * re-quantization). */
+svdq_status svdq_pack_weight(const svdq_layer_desc* d, const float* R, const uint16_t* L1,
+                             const uint16_t* L2, const float* lambda, const uint16_t* bias,
+                             void* w_packed, void* stream);
+
+/* Launch 1 (section 4.3: the down projection fused into the quantization kernel).
+ *   X        device, bf16 bits, M x K with row stride ldx
+ *   a_packed device, svdq_act_bytes(d, M) bytes, 256-byte aligned; receives the
+ *            packed codes and scales of X_hat = X / lambda and D = X_hat L1. */
+svdq_status svdq_quantize_act(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
+                              int64_t M, int64_t ldx, void* a_packed, void* stream);
+
+/* Launch 2 (section 4.3: the up projection fused into the 4-bit GEMM kernel).
+ *   Y  device, M x N with row stride ldy; bf16 bits, or float32 with
+ *      SVDQ_EPI_OUT_F32.  epi: OR of SVDQ_EPI_* flags. */
+svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void* a_packed,
+                      int64_t M, void* Y, int64_t ldy, uint32_t epi, void* stream);
+
+/* Both launches; workspace >= svdq_act_bytes(d, M) bytes (device, 256-aligned). */
+svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
+                        int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Test access to the opaque layouts, in canonical form (device outputs, any may be NULL):
+ *   codes   uint8 rows x K/2: two 4-bit codes per byte, element 2j in the low nibble
+ *           of byte j (INT4 codes as 4-bit two's complement)
+ *   scales  rows x K/32 uint8 E8M0 bytes (MXFP4) or rows x K/64 uint16 fp16 bits (INT4)
+ *   weight: L1 (K x rank bf16), L2 (rank x N bf16), lambda (float32[K]), bias (bf16[N])
+ *   act:    D (M x rank float32, the down projection as the GEMM epilogue consumes it) */
+svdq_status svdq_unpack_weight(const svdq_layer_desc* d, const void* w_packed, uint8_t* codes,
+                               void* scales, uint16_t* L1, uint16_t* L2, float* lambda,
+                               uint16_t* bias, void* stream);
+svdq_status svdq_unpack_act(const svdq_layer_desc* d, const void* a_packed, int64_t M,
+                            uint8_t* codes, void* scales, float* D, void* stream);
+
+/* Static string for a status code (never NULL). */
+const char* svdq_status_str(svdq_status s);
+
+/* SVDQ_OK if the current device is gfx950, else SVDQ_ERR_DEVICE. */
+svdq_status svdq_device_check(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int svdq_version(void);
+
+/* Test hook: with a nonzero argument every later device check reports
+ * SVDQ_ERR_DEVICE (until called again with 0), so that error path can be
+ * exercised on a machine whose GPU would pass the check.  Process-wide. */
+void svdq_test_force_device_error(int on);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -87,32 +87,30 @@ def forward(X_bits, lam, L1_bits, L2_bits, R_nk, b_bits, fmt: str, gelu_act: boo
 
 
 def forward_rows(X_bits, lam, L1_bits, L2_bits, R_nk, b_bits, fmt: str, rows, cols=None,
-                 gelu_act: bool = False, rq_cache: dict | None = None) -> np.ndarray:
-    """Y_o restricted to selected rows (and columns), for full-size checks.
-    The residual is quantized once (cached in rq_cache if given)."""
+                 gelu_act: bool = False) -> np.ndarray:
+    """Y_o restricted to selected rows and columns, for checks at full size.
+    Quantization is per row of X_hat and per output column of R, so only the
+    selected rows of X and of the N x K residual are quantized."""
     rows = np.asarray(rows)
-    if rq_cache is not None and "rq" in rq_cache:
-        rq = rq_cache["rq"]
-    else:
-        cR, sR = Q.quantize(np.asarray(R_nk, dtype=np.float32), fmt)
-        rq = Q.dequantize(cR, sR, fmt)
-        if rq_cache is not None:
-            rq_cache["rq"] = rq
+    R_nk = np.asarray(R_nk, dtype=np.float32)
+    if cols is not None:
+        cols = np.asarray(cols)
+        R_nk = R_nk[cols]
+    cR, sR = Q.quantize(R_nk, fmt)
+    rq = Q.dequantize(cR, sR, fmt)
     xhat = smooth(np.asarray(X_bits)[rows], lam)
     cX, sX = Q.quantize(xhat, fmt)
     xq = Q.dequantize(cX, sX, fmt)
-    if cols is not None:
-        rq = rq[np.asarray(cols)]
     y = xq @ rq.T
     if L1_bits is not None and np.asarray(L1_bits).shape[1] > 0:
         L2 = F.bf16_value(L2_bits)
         if cols is not None:
-            L2 = L2[:, np.asarray(cols)]
+            L2 = L2[:, cols]
         y = y + down_projection(xhat, L1_bits) @ L2
     if b_bits is not None:
         b = F.bf16_value(b_bits)
         if cols is not None:
-            b = b[np.asarray(cols)]
+            b = b[cols]
         y = y + b[None, :]
     return gelu(y) if gelu_act else y
 

@@ -47,7 +47,7 @@ def _groups(x: np.ndarray, g: int) -> np.ndarray:
     return x.reshape(x.shape[0], x.shape[1] // g, g)
 
 
-def mxfp4_quantize(x: np.ndarray, row_chunk: int = 4096):
+def mxfp4_quantize(x: np.ndarray, row_chunk: int = 1024):
     """x: float32 rows x K.  Returns (codes uint8 rows x K holding one E2M1
     nibble each, scales uint8 rows x K/32 holding E8M0 bytes)."""
     x = np.asarray(x, dtype=np.float32)
@@ -72,7 +72,7 @@ def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (vals * F.e8m0_value(scales)[..., None]).reshape(rows, K)
 
 
-def int4_quantize(x: np.ndarray, row_chunk: int = 4096):
+def int4_quantize(x: np.ndarray, row_chunk: int = 1024):
     """x: float32 rows x K.  Returns (codes int8 rows x K in [-8, 7],
     scales uint16 rows x K/64 holding fp16 bit patterns)."""
     x = np.asarray(x, dtype=np.float32)

@@ -36,10 +36,14 @@ import numpy as np
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Store float32 values as bf16 bit patterns, rounding to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    u = xf.view(np.uint32)
+    r = (u >> 16) & 1                      # no uint32 overflow for finite inputs
+    r += u
+    r += 0x7FFF
+    r >>= 16
     out = r.astype(np.uint16)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    nan = np.isnan(xf)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -209,13 +213,14 @@ def draw_layer(spec: LayerSpec, seed: Optional[int] = None, with_lora: bool = Tr
     # Residual: bulk-level Gaussian rows; non-absorbed heavy channels keep tails.
     rho = 0.02 * lam.astype(np.float64)
     rho[absorbed] = 0.02 * lam_base
-    z = rng.standard_normal((N, K))
+    z = rng.standard_normal((N, K), dtype=np.float32)
     heavy_left = np.setdiff1d(w_idx, absorbed)
     if heavy_left.size and spec.w_kind == "t3":
         z[:, heavy_left] = rng.standard_t(3.0, size=(N, heavy_left.size)) / math.sqrt(3.0)
     elif heavy_left.size:
         z[:, heavy_left] *= spec.w_factor
-    R = (z * rho[None, :]).astype(np.float32)
+    z *= rho.astype(np.float32)[None, :]
+    R = z
 
     # Low-rank factors: one column per absorbed channel carrying its magnified
     # row (scale = row magnitude * sqrt(N), unit-variance L2 row), then bulk

@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+layer through the C ABI, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import w4a4_quantized_linear_amd as sq
+from oracle import formats as F
+from oracle import layer as Ly
+from oracle import quant as Q
+
+
+def dev_tensor(a, torch, device):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def pack(layer, L, torch, device, bias=True):
+    return sq.pack_weight(layer, dev_tensor(L["R"], torch, device), dev_tensor(L["L1"], torch, device),
+                          dev_tensor(L["L2"], torch, device), dev_tensor(L["lam"], torch, device),
+                          dev_tensor(L["b"], torch, device) if bias else None)
+
+
+def scales_np(t, fmt):
+    a = t.cpu().numpy()
+    return a.view(np.uint8) if fmt == "mxfp4" else a.view(np.uint16)
+
+
+def bf16_to_np(t):
+    return F.bf16_value(t.cpu().view(__import__("torch").int16).numpy().view(np.uint16))
+
+
+def assert_codes_equal(got_packed, ref_codes, what):
+    ref = Q.pack_canonical(ref_codes)
+    if not np.array_equal(got_packed, ref):
+        bad = np.argwhere(got_packed != ref)
+        r, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} code bytes differ; first at row {r} byte {j}: "
+                             f"got {got_packed[r, j]:#04x} want {ref[r, j]:#04x}")
+
+
+def assert_scales_equal(got, ref, what):
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        r, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} scales differ; first at row {r} group {j}: "
+                             f"got {got[r, j]} want {ref[r, j]}")
+
+
+def bf16_half_ulp(y):
+    """Half a bf16 unit in the last place at each |y| (the output rounding allowance)."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))
+    return np.ldexp(1.0, e - 1 - 8)
+
+
+def check_fp32_output(Y, Y_o, what):
+    m = Ly.parity_metrics(Y, Y_o)
+    assert m["max_over_rms"] <= Ly.MAX_OVER_RMS and m["mean_rel"] <= Ly.MEAN_REL, f"{what}: {m}"
+    return m
+
+
+def check_bf16_output(Yb, Y_o, what):
+    """bf16 output: the stated tolerance plus the output format's own rounding
+    (half a bf16 ulp of each value), and the mean relative error bound."""
+    Yb = np.asarray(Yb, dtype=np.float64)
+    err = np.abs(Yb - Y_o)
+    rms = float(np.sqrt(np.mean(Y_o ** 2)))
+    lim = Ly.MAX_OVER_RMS * rms + bf16_half_ulp(Y_o)
+    assert np.all(err <= lim), f"{what}: max excess {(err - lim).max():.3e} (rms {rms:.3e})"
+    mean_rel = float(err.sum() / np.abs(Y_o).sum())
+    assert mean_rel <= Ly.MEAN_REL, f"{what}: mean rel {mean_rel:.3e}"
+    return mean_rel

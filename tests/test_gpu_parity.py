@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Element by element on seeded inputs at sizes the oracle finishes in seconds
+(several tiles, ragged M and N tails, rank 0 / 48 / 256, strided X, tiny and
+zero rows), and on sampled rows and columns at the full workload sizes in the
+launch configuration the benchmark times.  Codes and scales must be bit-exact;
+outputs within max|Y - Y_o| <= 2e-2 rms(Y_o) and mean relative error <= 5e-3
+(fp32 output), bf16 output adds half a bf16 ulp per value and must equal the
+round-to-nearest-even of the fp32 output.
+"""
+import numpy as np
+import pytest
+
+import synth
+import w4a4_quantized_linear_amd as sq
+from oracle import formats as F
+from oracle import layer as Ly
+from oracle import quant as Q
+
+from _gpu_helpers import (assert_codes_equal, assert_scales_equal, bf16_to_np, check_bf16_output,
+                          check_fp32_output, dev_tensor, pack, scales_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sq.lib()
+    assert sq.device_check(), "current device is not gfx950"
+    return torch, torch.device("cuda:0")
+
+
+# (name, fmt, M, K, N, rank, seed): ragged M/N tails, rank 0 .. 256, one row, minimum N
+MEDIUM = [
+    ("qkv", "mxfp4", 300, 1024, 512, 16, 1),
+    ("single", "int4", 300, 1024, 512, 16, 2),
+    ("qkv", "mxfp4", 1, 512, 256, 32, 3),
+    ("single", "int4", 17, 1536, 272, 0, 4),
+    ("lora", "mxfp4", 513, 2048, 784, 48, 5),
+    ("lowm", "mxfp4", 64, 512, 16, 256, 6),
+    ("lowm", "int4", 130, 512, 48, 128, 7),
+]
+
+
+def _medium_layer(name, fmt, M, K, N, rank, seed, edge=False):
+    spec = synth.layer_spec(name, M=M, K=K, N=N, rank=rank, fmt=fmt, x_outliers=max(1, K // 100),
+                            w_outliers=max(1, K // 100), lora_rank=0)
+    L = synth.draw_layer(spec, seed=seed)
+    if edge and M >= 4:
+        # edge rows: all zero, tiny (subnormal after smoothing), negative zeros, huge
+        X = L["X"].copy()
+        X[0] = 0
+        X[1] = synth.bf16_bits_from_f32(np.full(K, 3e-38, np.float32) * np.sign(np.arange(K) % 3 - 1))
+        X[2] = 0x8000
+        X[3, :7] = synth.bf16_bits_from_f32(np.array([3e37, -1e30, 1.0, -2.5, 0.0, 5e-39, 7.0], np.float32))
+        L["X"] = X
+    if edge and N >= 32:
+        R = L["R"].copy()
+        R[0] = 0.0
+        R[1, :5] = np.array([1e-40, -1e-41, 2e-39, 0.0, -0.0], np.float32)
+        L["R"] = R
+    return spec, L
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[f"{c[1]}-M{c[2]}-K{c[3]}-N{c[4]}-r{c[5]}" for c in MEDIUM])
+def test_layer_elementwise(torch_dev, case):
+    torch, dev = torch_dev
+    name, fmt, M, K, N, rank, seed = case
+    spec, L = _medium_layer(*case)
+    layer = sq.Layer(fmt, K, N, rank)
+    print(f"case {case}", flush=True)
+    w = pack(layer, L, torch, dev)
+    X = dev_tensor(L["X"], torch, dev)
+    ws = sq.quantize_act(layer, w, X)
+    uw = sq.unpack_weight(layer, w)
+    ua = sq.unpack_act(layer, ws, M)
+    Yf = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    Yb = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS)
+    Yg = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU | sq.EPI_OUT_F32)
+    Yl = sq.linear(layer, w, X, sq.EPI_LOWRANK | sq.EPI_BIAS)
+    torch.cuda.synchronize()
+
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], fmt)
+    # weights: codes and scales bit-exact, the 16-bit operands round-trip exactly
+    assert_codes_equal(uw["codes"].cpu().numpy(), ref["cR"], "weight codes")
+    assert_scales_equal(scales_np(uw["scales"], fmt), ref["sR"], "weight scales")
+    if rank:
+        assert np.array_equal(uw["L1"].cpu().numpy().view(np.uint16), L["L1"])
+        assert np.array_equal(uw["L2"].cpu().numpy().view(np.uint16), L["L2"])
+    assert np.array_equal(uw["lam"].cpu().numpy(), L["lam"])
+    assert np.array_equal(uw["bias"].cpu().numpy().view(np.uint16), L["b"])
+    # activations: codes and scales bit-exact
+    assert_codes_equal(ua["codes"].cpu().numpy(), ref["cX"], "activation codes")
+    assert_scales_equal(scales_np(ua["scales"], fmt), ref["sX"], "activation scales")
+    # down projection: hi/lo bf16 split of X_hat, fp32 accumulation
+    if rank:
+        Dg = ua["D"].cpu().numpy().astype(np.float64)
+        bound = np.abs(ref["xhat"].astype(np.float64)) @ np.abs(F.bf16_value(L["L1"]))
+        assert np.all(np.abs(Dg - ref["D"]) <= 2.0 ** -14 * bound + 1e-30), "down projection"
+    # outputs
+    Y_o = ref["Y"]
+    check_fp32_output(Yf.cpu().numpy(), Y_o, "fp32 output")
+    check_bf16_output(bf16_to_np(Yb), Y_o, "bf16 output")
+    # bf16 output is exactly the round-to-nearest-even of the fp32 output
+    assert np.array_equal(Yb.cpu().view(torch.int16).numpy().view(np.uint16), F.bf16_bits(Yf.cpu().numpy()))
+    # the two-launch entry point gives the same bytes
+    assert torch.equal(Yl.view(torch.int16), Yb.view(torch.int16))
+    check_fp32_output(Yg.cpu().numpy(), Ly.gelu(Y_o), "GELU output")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+def test_edge_values_bit_exact(torch_dev, fmt):
+    """Zero rows, signed zeros, subnormal inputs after smoothing, huge values:
+    codes and scales still match the oracle bit for bit."""
+    torch, dev = torch_dev
+    spec, L = _medium_layer("qkv", fmt, 40, 1024, 64, 16, 21, edge=True)
+    layer = sq.Layer(fmt, 1024, 64, 16)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    uw, ua = sq.unpack_weight(layer, w), sq.unpack_act(layer, ws, 40)
+    Y = sq.gemm(layer, w, ws, 40, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], fmt)
+    assert_codes_equal(uw["codes"].cpu().numpy(), ref["cR"], "weight codes")
+    assert_scales_equal(scales_np(uw["scales"], fmt), ref["sR"], "weight scales")
+    assert_codes_equal(ua["codes"].cpu().numpy(), ref["cX"], "activation codes")
+    assert_scales_equal(scales_np(ua["scales"], fmt), ref["sX"], "activation scales")
+    rows = np.arange(4, 40)                      # ordinary rows keep the stated tolerance
+    check_fp32_output(Y.cpu().numpy()[rows], ref["Y"][rows], "ordinary rows")
+    assert np.all(np.isfinite(Y.cpu().numpy()))
+
+
+def test_epilogue_flags_separately(torch_dev):
+    torch, dev = torch_dev
+    spec, L = _medium_layer("qkv", "mxfp4", 96, 1024, 256, 32, 11)
+    layer = sq.Layer("mxfp4", 1024, 256, 32)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    out = {e: sq.gemm(layer, w, ws, 96, e | sq.EPI_OUT_F32).cpu().numpy()
+           for e in (0, sq.EPI_LOWRANK, sq.EPI_BIAS, sq.EPI_LOWRANK | sq.EPI_BIAS)}
+    base = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4", with_lowrank=False,
+                      with_bias=False)["Y"]
+    lr = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4", with_bias=False)["Y"]
+    check_fp32_output(out[0], base, "4-bit branch only")
+    check_fp32_output(out[sq.EPI_LOWRANK], lr, "with low-rank")
+    diff = out[sq.EPI_BIAS].astype(np.float64) - out[0]
+    np.testing.assert_allclose(diff, np.broadcast_to(F.bf16_value(L["b"]), diff.shape), rtol=0,
+                               atol=2.0 ** -23 * np.abs(out[0]).max())
+
+
+def test_pack_without_bias_and_strided_x(torch_dev):
+    torch, dev = torch_dev
+    spec, L = _medium_layer("single", "int4", 50, 1024, 128, 16, 12)
+    layer = sq.Layer("int4", 1024, 128, 16)
+    w = pack(layer, L, torch, dev, bias=False)
+    wide = torch.zeros((50, 1024 + 64), dtype=torch.int16, device=dev)
+    wide[:, 32:32 + 1024] = dev_tensor(L["X"], torch, dev)
+    Xs = wide[:, 32:32 + 1024]                      # row stride 1088, 64-byte offset
+    Y = sq.linear(layer, w, Xs, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], None, "int4")["Y"]
+    check_fp32_output(Y.cpu().numpy(), ref, "no bias, strided X")
+
+
+def test_empty_batch_is_a_noop(torch_dev):
+    torch, dev = torch_dev
+    spec, L = _medium_layer("qkv", "mxfp4", 8, 512, 64, 16, 13)
+    layer = sq.Layer("mxfp4", 512, 64, 16)
+    w = pack(layer, L, torch, dev)
+    X = torch.empty((0, 512), dtype=torch.int16, device=dev)
+    Y = sq.linear(layer, w, X, sq.EPI_LOWRANK | sq.EPI_BIAS)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 64)
+
+
+def test_deterministic(torch_dev):
+    torch, dev = torch_dev
+    spec, L = _medium_layer("lora", "mxfp4", 700, 2048, 512, 48, 14)
+    layer = sq.Layer("mxfp4", 2048, 512, 48)
+    w = pack(layer, L, torch, dev)
+    X = dev_tensor(L["X"], torch, dev)
+    a = sq.linear(layer, w, X, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    b = sq.linear(layer, w, X, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_adapter_needs_no_requantization(torch_dev):
+    torch, dev = torch_dev
+    spec = synth.layer_spec("lora", M=256, K=1024, N=512)
+    L = synth.draw_layer(spec)
+    L0 = dict(L, L1=L["L1_svd"], L2=L["L2_svd"])
+    l48 = sq.Layer("mxfp4", 1024, 512, 48)
+    l32 = sq.Layer("mxfp4", 1024, 512, 32)
+    w48 = pack(l48, L, torch, dev)
+    w32 = pack(l32, L0, torch, dev)
+    u48, u32 = sq.unpack_weight(l48, w48), sq.unpack_weight(l32, w32)
+    assert torch.equal(u48["codes"], u32["codes"]) and torch.equal(u48["scales"], u32["scales"])
+    nbytes = 512 * 1024 // 2 + 512 * 1024 // 32       # code and scale sections lead the blob
+    assert torch.equal(w48[:nbytes], w32[:nbytes])
+    Y = sq.linear(l48, w48, dev_tensor(L["X"], torch, dev), sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")["Y"]
+    check_fp32_output(Y.cpu().numpy(), ref, "adapter-stacked layer")
+
+
+def test_device_error_path_on_gpu(torch_dev):
+    torch, dev = torch_dev
+    layer = sq.Layer("mxfp4", 512, 64, 16)
+    w = torch.zeros(sq.weight_bytes(layer), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(sq.act_bytes(layer, 4), dtype=torch.uint8, device=dev)
+    Y = torch.full((4, 64), 7, dtype=torch.int16, device=dev)
+    sq.lib().svdq_test_force_device_error(1)
+    try:
+        with pytest.raises(sq.SvdqError) as e:
+            sq.gemm(layer, w, ws, 4, 0, out=Y)
+        assert e.value.status == 6
+    finally:
+        sq.lib().svdq_test_force_device_error(0)
+    torch.cuda.synchronize()
+    assert bool((Y == 7).all())                      # outputs untouched on error
+    with pytest.raises(sq.SvdqError) as e:
+        sq.linear(layer, w, torch.zeros((4, 512), dtype=torch.int16, device=dev), 0,
+                  workspace=ws[:ws.numel() - 256])
+    assert e.value.status == 5

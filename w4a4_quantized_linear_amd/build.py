@@ -1,0 +1,56 @@
+"""Build libsvdq.so in-tree with hipcc for gfx950.
+
+Usage: python -m w4a4_quantized_linear_amd.build   (or __graft_entry__.build()).
+Always recompiles.  Flags: -O3, IEEE-correct fp32 division and denormals
+(hipcc's defaults; never fast-math), packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libsvdq.so")
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def flags() -> list:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-fno-gpu-rdc", "-Wall", "-Wno-unused-function",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    ]
+
+
+def build(verbose: bool = True) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

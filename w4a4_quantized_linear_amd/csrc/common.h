@@ -1,0 +1,91 @@
+// Device helpers shared by the kernels: vector types, bf16/fp16 conversions and
+// the MFMA wrappers.  gfx950 only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace svdq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// bf16 bits <-> fp32
+__device__ __forceinline__ float bf_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+
+// The E8M0 exponent byte of a group maximum: e = floor(log2 amax) - 2 clamped to
+// [-127, 127], stored as e + 127.  For a normal amax with biased exponent be this is
+// be - 2 (at least 0); zero and subnormal maxima give byte 0 (e = -127).
+__device__ __forceinline__ uint32_t e8m0_of_amax(float amax) {
+  const int be = int((__float_as_uint(amax) >> 23) & 0xFFu);
+  return uint32_t(be > 2 ? be - 2 : 0);
+}
+// 2^-e as fp32 for a scale byte b (e = b - 127); exact for every b in [0, 254].
+__device__ __forceinline__ float inv_scale_of_e8m0(uint32_t b) {
+  // 2^(127 - b) has biased exponent 254 - b; scale bytes from e8m0_of_amax are at
+  // most 252, so the result is a normal power of two in [2^-125, 2^127].
+  return __uint_as_float((254u - b) << 23);
+}
+
+// Two fp32 -> packed E2M1 pair in byte `sel` of `old` (nearest, ties to even,
+// saturating at 6, sign copied): the gfx950 convert with unit scale.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f c, uint32_t sa, uint32_t sb) {
+  v8i av = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
+  v8i bv = {int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL, int(sa), SEL, int(sb));
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const uint4& a, const uint4& b, v4f c) {
+  v8s as = {short(a.x), short(a.x >> 16), short(a.y), short(a.y >> 16),
+            short(a.z), short(a.z >> 16), short(a.w), short(a.w >> 16)};
+  v8s bs = {short(b.x), short(b.x >> 16), short(b.y), short(b.y >> 16),
+            short(b.z), short(b.z >> 16), short(b.w), short(b.w >> 16)};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, as), __builtin_bit_cast(v8bf, bs), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4i mfma_i8(const v4i& a, const v4i& b) {
+  v4i z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, z, 0, 0, 0);
+}
+
+// 8 packed two's complement nibbles -> 8 signed bytes in two dwords
+// (even elements in the first, odd in the second).  Per byte, with x the nibble:
+// ((x ^ 8) + 0x78) ^ 0x80 is x sign-extended, with no carry between bytes.
+__device__ __forceinline__ void unpack_i4x8(uint32_t d, int& even, int& odd) {
+  const uint32_t lo = d & 0x0F0F0F0Fu;
+  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
+  even = int(((lo ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
+  odd = int(((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
+}
+
+__device__ __forceinline__ float gelu_erf(float y) { return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f)); }
+
+// Hardware round-robins workgroups over the 8 XCDs (workgroup i runs on XCD i % 8).
+// Map the dispatch index to a logical tile index so that each XCD works on a
+// contiguous range of tiles (and so shares operands in its own L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int nx = 8;
+  const int xcd = bid % nx, slot = bid / nx;
+  const int per = nblocks / nx, rem = nblocks % nx;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace svdq

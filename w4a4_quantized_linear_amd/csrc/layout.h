@@ -1,0 +1,137 @@
+// Physical layouts of the packed weight blob and the activation workspace.
+//
+// Everything the GEMM reads is stored in the order one MFMA operand fragment is
+// consumed, so each fragment is one fully coalesced 1 KiB load (64 lanes x 16 B)
+// and no shuffling happens in the hot loop.
+//
+// Scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), per 16-row x 128-K tile:
+//   lane L holds row (L % 16) and the 32-element K block (L / 16): 16 bytes,
+//   element t of the block in byte t/2 (low nibble for even t).  The E8M0 scale
+//   of that (row, block) is one byte of a per-lane 32-bit scale register.
+//   Scale "superfragment" per 16 rows x 512 K: lane L's dword holds, in byte j,
+//   the scale of row L%16, block L/16 of the 128-K step j.
+// INT8 MFMA (v_mfma_i32_16x16x64_i8) for INT4: per 16-row x 128-K tile, lane L
+//   holds row L%16 and, for both 64-element groups g of the tile, the 16 codes
+//   at group offset (L/16)*16: bytes [8g, 8g+8) = 16 nibbles.  Scales: per 128-K
+//   step and row, two fp16 (groups 0 and 1) in 4 bytes, rows contiguous.
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16) fragments for the low-rank branch: lane
+//   L holds row/column L%16 and 8 consecutive K (rank) elements at (L/16)*8.
+//
+// Both operands use the same in-lane element order, so the product is the dot
+// product over each K block regardless of that order.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace svdq {
+
+constexpr int kTileRows = 256;     // rows of N (weights) and M (activations) are padded to this
+constexpr int kKStep = 128;        // K per MFMA step
+constexpr int kKSuper = 512;       // K per scale superfragment; K must be a multiple
+constexpr int kRankAlign = 32;     // rank padded to the bf16 MFMA K
+constexpr int kFmtMXFP4 = 1;
+constexpr int kFmtINT4 = 2;
+
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
+
+struct WeightLayout {
+  int64_t N_pad, r_pad;
+  size_t codes, scales, L1, L2, lam, rlam, bias, total;
+};
+
+struct ActLayout {
+  int64_t M_pad, r_pad;
+  size_t codes, scales, D, total;
+};
+
+// Codes: N_pad x K/2 bytes.  Scales: N_pad x K/32 bytes (E8M0 per 32, or fp16 per 64).
+// L1: K x r_pad bf16 (B fragments of the down projection).  L2: N_pad x r_pad bf16
+// (A fragments of the up projection).  lambda and 1/lambda: fp32[K].  bias: bf16[N_pad].
+__host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
+  WeightLayout w;
+  w.N_pad = round_up(N, kTileRows);
+  w.r_pad = round_up(rank, kRankAlign);
+  size_t o = 0;
+  w.codes = o;  o = align256(o + size_t(w.N_pad) * K / 2);
+  w.scales = o; o = align256(o + size_t(w.N_pad) * K / 32);
+  w.L1 = o;     o = align256(o + size_t(K) * w.r_pad * 2);
+  w.L2 = o;     o = align256(o + size_t(w.N_pad) * w.r_pad * 2);
+  w.lam = o;    o = align256(o + size_t(K) * 4);
+  w.rlam = o;   o = align256(o + size_t(K) * 4);
+  w.bias = o;   o = align256(o + size_t(w.N_pad) * 2);
+  w.total = o;
+  return w;
+}
+
+// Codes: M_pad x K/2.  Scales: M_pad x K/32 bytes.  D: M_pad x r_pad x {hi, lo} bf16.
+__host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
+  ActLayout a;
+  a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
+  a.r_pad = round_up(rank, kRankAlign);
+  size_t o = 0;
+  a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
+  a.scales = o; o = align256(o + size_t(a.M_pad) * K / 32);
+  a.D = o;      o = align256(o + size_t(a.M_pad) * a.r_pad * 4);
+  a.total = o;
+  return a;
+}
+
+// ---- codes: byte offset of the 16-byte lane chunk of tile (rt, ks), lane L ----
+__host__ __device__ inline size_t code_chunk(int64_t rt, int ks, int K, int L) {
+  return (size_t(rt) * (K / kKStep) + ks) * 1024 + size_t(L) * 16;
+}
+
+// Canonical (row, k) -> (byte offset, high-nibble?) in the code section.
+__host__ __device__ inline size_t code_byte(int fmt, int64_t row, int k, int K, int* hi) {
+  const int64_t rt = row / 16;
+  const int r = int(row % 16);
+  const int ks = k / kKStep;
+  const int kk = k % kKStep;
+  if (fmt == kFmtMXFP4) {
+    const int blk = kk / 32, t = kk % 32;
+    *hi = t & 1;
+    return code_chunk(rt, ks, K, blk * 16 + r) + t / 2;
+  }
+  const int g = kk / 64, o = kk % 64, c = o / 16, t = o % 16;
+  *hi = t & 1;
+  return code_chunk(rt, ks, K, c * 16 + r) + g * 8 + t / 2;
+}
+
+// ---- scales ----
+// MXFP4: byte offset of the scale of (row, 32-block index kb) (kb = k / 32).
+__host__ __device__ inline size_t mx_scale_byte(int64_t row, int kb, int K) {
+  const int64_t rt = row / 16;
+  const int r = int(row % 16);
+  const int ks = kb / 4, blk = kb % 4;          // 128-K step and block within it
+  const int sup = ks / 4, j = ks % 4;           // superfragment and byte within the dword
+  return ((size_t(rt) * (K / kKSuper) + sup) * 64 + (blk * 16 + r)) * 4 + j;
+}
+// INT4: byte offset of the fp16 scale of (row, 64-group index g) with rows padded to rows_pad.
+__host__ __device__ inline size_t i4_scale_byte(int64_t row, int g, int64_t rows_pad) {
+  const int ks = g / 2, h = g % 2;
+  return ((size_t(ks) * rows_pad + row) * 2 + h) * 2;
+}
+
+// ---- low-rank fragments (bf16 element offsets) ----
+// L1 (K x r_pad): B fragment of the down projection, tile (k32, i16), lane L, element e:
+//   k = k32*32 + (L/16)*8 + e, i = i16*16 + L%16.
+__host__ __device__ inline size_t l1_elem(int k, int i, int r_pad) {
+  const int k32 = k / 32, kk = k % 32, i16 = i / 16, L = (kk / 8) * 16 + (i % 16), e = kk % 8;
+  return ((size_t(k32) * (r_pad / 16) + i16) * 64 + L) * 8 + e;
+}
+// L2 (N_pad x r_pad): A fragment of the up projection, tile (n16, r32), lane L, element e:
+//   n = n16*16 + L%16, rank = r32*32 + (L/16)*8 + e.
+__host__ __device__ inline size_t l2_elem(int64_t n, int rk, int r_pad) {
+  const int64_t n16 = n / 16;
+  const int r32 = rk / 32, kk = rk % 32, L = (kk / 8) * 16 + int(n % 16), e = kk % 8;
+  return ((size_t(n16) * (r_pad / 32) + r32) * 64 + L) * 8 + e;
+}
+// D (M_pad x r_pad, hi/lo bf16): B fragment of the up projection, tile (m16, r32), part h.
+__host__ __device__ inline size_t d_elem(int64_t m, int rk, int h, int r_pad) {
+  const int64_t m16 = m / 16;
+  const int r32 = rk / 32, kk = rk % 32, L = (kk / 8) * 16 + int(m % 16), e = kk % 8;
+  return (((size_t(m16) * (r_pad / 32) + r32) * 2 + h) * 64 + L) * 8 + e;
+}
+
+}  // namespace svdq
