@@ -1,0 +1,219 @@
+"""Benchmark: effective TOPS of the fused W4A4 + low-rank linear on FLUX shapes.
+
+One step = the FLUX-shaped MLP pair in MXFP4, every launch of the hot path:
+  fc1: svdq_quantize_act + svdq_gemm (M=4608, K=3072 -> N=12288, r=32, GELU fused)
+  fc2: svdq_quantize_act + svdq_gemm (M=4608, K=12288 -> N=3072, r=32)
+on synthetic seeded inputs already resident in HBM (weights packed once before
+timing, as at load time).  value = (2 M N K of fc1 + of fc2) per step / time.
+
+Prints one JSON line.  `roofline` is the fc1 GEMM kernel (the dominant launch),
+timed with HIP events around each of its launches inside the timed region.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS of fused W4A4+low-rank linear, FLUX shapes; % of FP4 MFMA peak"
+PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 5000.0}          # MI355X dense FP4 / INT8 MFMA
+PAIRS = {
+    "mlp_mxfp4": ("fc1_mxfp4", "fc2_mxfp4"),
+    "mlp_int4": ("fc1_int4", "fc2_int4"),
+}
+SINGLE = ("qkv", "lowm", "lora", "single")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def layers_of(workload):
+    import synth
+    names = PAIRS.get(workload, (workload,))
+    return [synth.CONFIGS[n] for n in names]
+
+
+def gemm_source_hash() -> str:
+    with open(os.path.join(ROOT, "w4a4_quantized_linear_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current GEMM source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        e = d.get(f"{workload}:{kernel}")
+        if e and e.get("gemm_source_sha256_16") == gemm_source_hash():
+            return e.get("bytes_per_launch")
+    except (ValueError, OSError):
+        return None
+    return None
+
+
+def gpu_leg(args):
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a4_quantized_linear_amd as sq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    specs = layers_of(args.workload)
+    layers, weights, inputs = [], [], []
+    for i, spec in enumerate(specs):
+        L = synth.draw_layer(spec)
+        r = spec.rank + spec.lora_rank
+        layer = sq.Layer(spec.fmt, spec.K, spec.N, r)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+        w = sq.pack_weight(layer, t(L["R"]), t(L["L1"]), t(L["L2"]), t(L["lam"]), t(L["b"]))
+        layers.append(layer)
+        weights.append(w)
+        inputs.append(t(L["X"]) if i == 0 else None)
+        del L
+    M = specs[0].M
+    ws = [torch.empty(sq.act_bytes(l, M), dtype=torch.uint8, device=dev) for l in layers]
+    outs = [torch.empty((M, l.N), dtype=torch.bfloat16, device=dev) for l in layers]
+    epis = [sq.EPI_LOWRANK | sq.EPI_BIAS | (sq.EPI_GELU if s.gelu else 0) for s in specs]
+    torch.cuda.synchronize()
+
+    n = len(layers)
+
+    def step(ev=None):
+        x = inputs[0]
+        for i in range(n):
+            if ev is not None:
+                ev[i][0].record()
+            sq.quantize_act(layers[i], weights[i], x, out=ws[i])
+            if ev is not None:
+                ev[i][1].record()
+            sq.gemm(layers[i], weights[i], ws[i], M, epis[i], out=outs[i])
+            if ev is not None:
+                ev[i][2].record()
+            x = outs[i].view(torch.int16)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(stop)
+
+    quant_us = [sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) * 1e3 / args.steps
+                for i in range(n)]
+    gemm_us = [sum(evs[k][i][1].elapsed_time(evs[k][i][2]) for k in range(args.steps)) * 1e3 / args.steps
+               for i in range(n)]
+    flops = [2.0 * M * s.N * s.K for s in specs]
+    ms_per_step = wall * 1e3 / args.steps
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the GEMM with the most work (fc1 for the MLP pair)
+    i_dom = max(range(n), key=lambda i: gemm_us[i])
+    fmt = specs[i_dom].fmt
+    achieved = flops[i_dom] / (gemm_us[i_dom] * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[fmt]
+    kname = f"gemm_{fmt}_{specs[i_dom].name}"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(kname, args.workload),
+                "kernel": kname, "flops_per_launch": flops[i_dom], "avg_launch_us": round(gemm_us[i_dom], 2)}
+    breakdown = {}
+    for i, s in enumerate(specs):
+        hbm_q = 2 * M * s.K + M * s.K // 2 + M * s.K // 32 + 4 * M * layers[i].rank + 2 * s.K * layers[i].rank
+        breakdown[s.name] = {
+            "quantize_us": round(quant_us[i], 2),
+            "quantize_GBps": round(hbm_q / (quant_us[i] * 1e-6) / 1e9, 1),
+            "gemm_us": round(gemm_us[i], 2),
+            "gemm_TFLOPs": round(flops[i] / (gemm_us[i] * 1e-6) / 1e12, 1),
+            "linear_TOPS": round(flops[i] / ((gemm_us[i] + quant_us[i]) * 1e-6) / 1e12, 1),
+        }
+    return dict(value=value, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps, roofline=roofline,
+                breakdown=breakdown, specs=specs, fmt=specs[0].fmt)
+
+
+def cpu_baseline(specs, budget_rows=256):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    `budget_rows` tokens of each layer against 1/4 (fc1-sized layers) or 1/16 of
+    the output columns, scaled to effective TOPS of the sampled work."""
+    import numpy as np
+
+    import synth
+    from oracle import layer as Ly
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - optional dependency
+        threads = 1
+    work, secs, parts = 0.0, 0.0, []
+    for spec in specs:
+        L = synth.draw_layer(spec)
+        r = spec.rank + spec.lora_rank
+        rows = np.arange(min(budget_rows, spec.M))
+        ncols = max(16, spec.N // (4 if spec.K <= 4096 else 16))
+        cols = np.arange(ncols)
+        t0 = time.perf_counter()
+        Ly.forward_rows(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], spec.fmt, rows, cols,
+                        gelu_act=spec.gelu)
+        secs += time.perf_counter() - t0
+        work += 2.0 * rows.size * ncols * spec.K
+        parts.append(f"{spec.name}: {rows.size} tokens x {ncols} outputs (K={spec.K}, r={r})")
+        del L
+    return {"value": round(work / secs / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": "; ".join(parts) + f"; {secs:.1f} s of oracle time (quantize both operands, fp64 product, "
+                      "low-rank branch, bias, GELU); quantization is single-threaded numpy, the product uses "
+                      f"{threads} BLAS threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the layer is single-GPU; see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    r = gpu_leg(args)
+    specs = r["specs"]
+    cfg = {"workload": args.workload, "layers": [
+        {"name": s.name, "M": s.M, "K": s.K, "N": s.N, "rank": s.rank + s.lora_rank, "fmt": s.fmt,
+         "epilogue": "lowrank+bias" + ("+gelu" if s.gelu else "")} for s in specs],
+        "output": "bf16", "weights": "packed once before timing"}
+    line = {
+        "metric": METRIC, "value": round(r["value"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": r["fmt"], "data": "synthetic",
+        "config": cfg, "roofline": r["roofline"], "breakdown": r["breakdown"],
+        "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(specs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,7 +12,7 @@ from oracle import layer as Ly
 from oracle import quant as Q
 
 from _gpu_helpers import (assert_codes_equal, assert_scales_equal, bf16_to_np, check_bf16_output,
-                          check_fp32_output, dev_tensor, pack, scales_np)
+                          check_chain_output, check_fp32_output, dev_tensor, pack, scales_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,4 +89,4 @@ def test_mlp_pair_chain(torch_dev, fmt):
     H_o = F.bf16_bits(Y1_o)
     check_bf16_output(bf16_to_np(H), Y1_o, "fc1 + GELU")
     Y2_o = Ly.forward(H_o, L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], fmt)["Y"]
-    check_fp32_output(Y2.cpu().numpy(), Y2_o, "MLP pair output")
+    check_chain_output(Y2.cpu().numpy(), Y2_o, "MLP pair output")

@@ -55,6 +55,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m w4a4_quantized_linear_amd.build`")
+        _warn_if_stale()
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)
@@ -62,6 +63,20 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+def _warn_if_stale() -> None:
+    """Loud warning when the built library does not match the current sources."""
+    import sys
+    try:
+        from .build import source_hash
+        with open(LIB_PATH + ".srchash") as f:
+            built = f.read().strip()
+        if built != source_hash():
+            print(f"WARNING: {LIB_PATH} was built from other sources than the ones in the tree; "
+                  "rebuild with `python -m w4a4_quantized_linear_amd.build`", file=sys.stderr, flush=True)
+    except OSError:
+        print(f"WARNING: no source hash next to {LIB_PATH}; it may be stale", file=sys.stderr, flush=True)
 
 
 def check(fn: str, status: int) -> None:

@@ -35,6 +35,18 @@ def flags() -> list:
     ]
 
 
+def source_hash() -> str:
+    """Hash of every source the library is built from (kept beside the .so)."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h")):
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = True) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
@@ -48,6 +60,8 @@ def build(verbose: bool = True) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
+    with open(LIB + ".srchash", "w") as f:
+        f.write(source_hash())
     return LIB
 
 
