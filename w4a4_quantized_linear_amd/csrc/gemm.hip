@@ -93,39 +93,85 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 }
 
 // ------------------------------------------------------------------ MXFP4
+//
+// 256 threads = 4 waves (1 per SIMD, so each has the full register file), workgroup
+// tile 256 (n) x 256 (m), wave tile 128 (n) x 128 (m) = 8 x 8 MFMA blocks with the
+// accumulators in AGPRs.  Per 128-K step a stage holds 16 weight and 16 activation
+// fragments (32 KiB); each wave fetches 8 of them with buffer loads two steps
+// ahead into one of two register staging sets, writes them to one of two LDS
+// buffers one step ahead, and computes from the other.  The E8M0 scales of a
+// 512-K superfragment (one dword per lane and 16-row tile) are loaded into
+// registers one superfragment ahead; the MFMA of step u of the superfragment
+// picks byte u of the dword.
+//
+// Step t (buffer t % 2):  issue loads of step t+2 into staging set t % 2;
+// compute step t from LDS buffer t % 2; write staging set (t+1) % 2 (step t+1)
+// into LDS buffer (t+1) % 2; wait for the LDS writes; barrier.  The barrier uses
+// no memory fence, which would also wait for the loads still in flight.
 
-template <int TT, int WN, int WM>
-__device__ __forceinline__ void fp4_kstep(v4f (&acc)[WN][WM], uint4 (&a)[2][WN], uint4 (&b)[2][WM],
-                                          const uint32_t (&sa)[WN], const uint32_t (&sb)[WM], const uint4* Wc,
-                                          const uint4* Ac, int KS, int ks) {
-  constexpr int cur = TT & 1, nxt = cur ^ 1;
-  if (ks + 1 < KS) {
+constexpr int kStageFrags = 16;                 // fragments per operand per stage
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
+
+// Buffer resource over [base, base + bytes): loads beyond the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
+}
+
+// Wait for this wave's LDS operations, then a workgroup barrier without a memory
+// fence; the empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x0 << 8) | 0xF | (0x3 << 14));   // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int U, int WN, int WM>
+__device__ __forceinline__ void fp4_mma_stage(v4f (&acc)[WN][WM], const uint4* A, const uint4* B,
+                                              const uint32_t (&sa)[WN], const uint32_t (&sb)[WM], int lane) {
+  // all fragment reads first, so their latency overlaps the first MFMAs
+  uint4 af[WN], bf[WM];
 #pragma unroll
-    for (int i = 0; i < WN; ++i) a[nxt][i] = Wc[(size_t(i) * KS + ks + 1) * 64];
+  for (int j = 0; j < WM; ++j) bf[j] = B[j * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < WM; ++j) b[nxt][j] = Ac[(size_t(j) * KS + ks + 1) * 64];
-  }
+  for (int i = 0; i < WN; ++i) af[i] = A[i * 64 + lane];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = mfma_fp4_sel<TT>(a[cur][i], b[cur][j], acc[i][j], sa[i], sb[j]);
+    for (int j = 0; j < WM; ++j) acc[i][j] = mfma_fp4_sel<U>(af[i], bf[j], acc[i][j], sa[i], sb[j]);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int WN, int WM, bool OUT_F32>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
+  __shared__ uint4 la0[kStageFrags * 64], la1[kStageFrags * 64];
+  __shared__ uint4 lb0[kStageFrags * 64], lb1[kStageFrags * 64];
+  static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = w & 1, wm = w >> 1;               // 2 x 2 waves
+  constexpr int BN = 256, BM = 256;
   const int tiles_m = int(g.M_pad / BM);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = t % tiles_m, tn = t / tiles_m;
-  const int64_t n0 = int64_t(tn) * BN + (w & 1) * (WN * 16);
-  const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
+  const int64_t nt0 = int64_t(tn) * (BN / 16);    // first 16-row weight tile of the workgroup
+  const int64_t mt0 = int64_t(tm) * (BM / 16);
   const int KS = g.K / kKStep, KSUP = g.K / kKSuper;
 
-  const uint4* Wc = reinterpret_cast<const uint4*>(g.wblob + g.w_codes) + (n0 / 16) * KS * 64 + lane;
-  const uint4* Ac = reinterpret_cast<const uint4*>(g.act + g.a_codes) + (m0 / 16) * KS * 64 + lane;
-  const uint32_t* Ws = reinterpret_cast<const uint32_t*>(g.wblob + g.w_scales) + (n0 / 16) * KSUP * 64 + lane;
-  const uint32_t* As = reinterpret_cast<const uint32_t*>(g.act + g.a_scales) + (m0 / 16) * KSUP * 64 + lane;
+  // Per-workgroup views of the operands: 16 row tiles of codes and of scales each.
+  const uint32_t code_bytes = uint32_t(kStageFrags) * KS * 1024, scale_bytes = uint32_t(kStageFrags) * KSUP * 256;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.wblob + g.w_codes + size_t(nt0) * KS * 1024, code_bytes);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.act + g.a_codes + size_t(mt0) * KS * 1024, code_bytes);
+  const __amdgpu_buffer_rsrc_t rSA = make_rsrc(g.wblob + g.w_scales + size_t(nt0) * KSUP * 256, scale_bytes);
+  const __amdgpu_buffer_rsrc_t rSB = make_rsrc(g.act + g.a_scales + size_t(mt0) * KSUP * 256, scale_bytes);
+  const uint32_t voff16 = uint32_t(lane) * 16, voff4 = uint32_t(lane) * 4;
+  uint4* const la[2] = {la0, la1};
+  uint4* const lb[2] = {lb0, lb1};
 
   v4f acc[WN][WM];
 #pragma unroll
@@ -133,30 +179,74 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 a[2][WN], b[2][WM];
+  // E8M0 scales of this wave's 8 weight tiles and 8 activation tiles, one superfragment
   uint32_t sa[WN], sb[WM], san[WN], sbn[WM];
+  auto load_scales = [&](uint32_t (&x)[WN], uint32_t (&y)[WM], int sup) {
 #pragma unroll
-  for (int i = 0; i < WN; ++i) { a[0][i] = Wc[size_t(i) * KS * 64]; sa[i] = Ws[size_t(i) * KSUP * 64]; }
+    for (int i = 0; i < WN; ++i)
+      x[i] = __builtin_amdgcn_raw_buffer_load_b32(rSA, voff4, uint32_t((wn * WN + i) * KSUP + sup) * 256, 0);
 #pragma unroll
-  for (int j = 0; j < WM; ++j) { b[0][j] = Ac[size_t(j) * KS * 64]; sb[j] = As[size_t(j) * KSUP * 64]; }
-
-  for (int sup = 0; sup < KSUP; ++sup) {
-    const int ks = sup * 4;
-    if (sup + 1 < KSUP) {
+    for (int j = 0; j < WM; ++j)
+      y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WM + j) * KSUP + sup) * 256, 0);
+  };
+  // this wave's share of a stage: fragments 4w .. 4w+3 of each operand
+  uint4 stA[2][4], stB[2][4];
+  auto fetch = [&](int step, uint4 (&xa)[4], uint4 (&xb)[4]) {
 #pragma unroll
-      for (int i = 0; i < WN; ++i) san[i] = Ws[(size_t(i) * KSUP + sup + 1) * 64];
-#pragma unroll
-      for (int j = 0; j < WM; ++j) sbn[j] = As[(size_t(j) * KSUP + sup + 1) * 64];
+    for (int f = 0; f < 4; ++f) {
+      const uint32_t so = uint32_t((4 * w + f) * KS + step) * 1024;
+      xa[f] = load_frag(rA, voff16, so);
+      xb[f] = load_frag(rB, voff16, so);
     }
-    fp4_kstep<0>(acc, a, b, sa, sb, Wc, Ac, KS, ks + 0);
-    fp4_kstep<1>(acc, a, b, sa, sb, Wc, Ac, KS, ks + 1);
-    fp4_kstep<2>(acc, a, b, sa, sb, Wc, Ac, KS, ks + 2);
-    fp4_kstep<3>(acc, a, b, sa, sb, Wc, Ac, KS, ks + 3);
+  };
+  auto stash = [&](const uint4 (&xa)[4], const uint4 (&xb)[4], int buf) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      la[buf][(4 * w + f) * 64 + lane] = xa[f];
+      lb[buf][(4 * w + f) * 64 + lane] = xb[f];
+    }
+  };
+
+  // prologue: scales of superfragment 0; stage 0 into LDS buffer 0; stage 1 in flight
+  load_scales(sa, sb, 0);
+  fetch(0, stA[0], stB[0]);
+  fetch(1, stA[1], stB[1]);
+  stash(stA[0], stB[0], 0);
+  lds_barrier();
+
+  // Steady state: every step fetches two ahead and stashes one ahead; the last
+  // superfragment is peeled so the loop body has no branches.
+#define SVDQ_FP4_STEP(U, FETCH, STASH)                                                                \
+  {                                                                                                   \
+    if (FETCH) fetch(t0 + (U) + 2, stA[(U) & 1], stB[(U) & 1]);                                      \
+    if ((U) == 1 && (FETCH) && sup + 1 < KSUP) load_scales(san, sbn, sup + 1);                       \
+    __builtin_amdgcn_sched_barrier(0); /* keep the prefetch at the top of the step */                 \
+    fp4_mma_stage<(U)>(acc, la[(U) & 1] + (wn * WN) * 64, lb[(U) & 1] + (wm * WM) * 64, sa, sb, lane); \
+    if (STASH) stash(stA[((U) + 1) & 1], stB[((U) + 1) & 1], ((U) + 1) & 1);                        \
+    lds_barrier();                                                                                    \
+  }
+  int sup = 0;
+  for (; sup + 1 < KSUP; ++sup) {
+    const int t0 = sup * 4;
+    SVDQ_FP4_STEP(0, true, true)
+    SVDQ_FP4_STEP(1, true, true)
+    SVDQ_FP4_STEP(2, true, true)
+    SVDQ_FP4_STEP(3, true, true)
 #pragma unroll
     for (int i = 0; i < WN; ++i) sa[i] = san[i];
 #pragma unroll
     for (int j = 0; j < WM; ++j) sb[j] = sbn[j];
   }
+  {
+    const int t0 = sup * 4;
+    SVDQ_FP4_STEP(0, true, true)
+    SVDQ_FP4_STEP(1, true, true)
+    SVDQ_FP4_STEP(2, false, true)
+    SVDQ_FP4_STEP(3, false, false)
+  }
+#undef SVDQ_FP4_STEP
+  const int64_t n0 = (nt0 + wn * WN) * 16;
+  const int64_t m0 = (mt0 + wm * WM) * 16;
   epilogue<WN, WM, OUT_F32>(g, acc, n0, m0, lane);
 }
 
@@ -249,12 +339,11 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
   g.Y = Y;
   const bool f32 = (epi & SVDQ_EPI_OUT_F32) != 0;
   if (fmt == kFmtMXFP4) {
-    constexpr int WN = 8, WM = 4;
-    const unsigned nb = unsigned((wl.N_pad / (2 * WN * 16)) * (al.M_pad / (2 * WM * 16)));
+    const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
     if (f32)
-      hipLaunchKernelGGL((gemm_mxfp4_kernel<WN, WM, true>), dim3(nb), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true>), dim3(nb), dim3(256), 0, s, g);
     else
-      hipLaunchKernelGGL((gemm_mxfp4_kernel<WN, WM, false>), dim3(nb), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false>), dim3(nb), dim3(256), 0, s, g);
   } else {
     constexpr int WN = 4, WM = 4;
     const unsigned nb = unsigned((wl.N_pad / (2 * WN * 16)) * (al.M_pad / (2 * WM * 16)));
