@@ -5,7 +5,7 @@
 #include <atomic>
 #include <cstring>
 
-#include "../../include/svdq.h"
+#include "svdq.h"
 #include "layout.h"
 
 namespace svdq {

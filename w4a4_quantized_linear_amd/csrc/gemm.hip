@@ -18,7 +18,7 @@
 // then int32 -> fp32 times sW * sX accumulated in fp32.
 #include <hip/hip_runtime.h>
 
-#include "../../include/svdq.h"
+#include "svdq.h"
 #include "common.h"
 
 namespace svdq {
@@ -35,9 +35,33 @@ struct GemmArgs {
 };
 
 // ------------------------------------------------------------------ epilogue
+//
+// Low-rank MFMAs first (their operand loads come before any store), then every
+// bias value the wave needs, then bias + activation + conversion + stores with no
+// loads in between: on this architecture the vector-memory counter also counts
+// stores, so a load waited on inside the store sequence would wait for the stores.
+// A wave tile entirely inside Y takes the store path without per-block checks.
 
 template <int WN, int WM, bool OUT_F32>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane) {
+__device__ __forceinline__ void store_block(const GemmArgs& g, int64_t m, int64_t n, const float (&y)[4]) {
+  if (OUT_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.Y) + m * g.ldy + n) = make_float4(y[0], y[1], y[2], y[3]);
+  } else {
+    uint2 o;
+    o.x = pack_bf2(y[0], y[1]);
+    o.y = pack_bf2(y[2], y[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.Y) + m * g.ldy + n) = o;
+  }
+}
+
+// bf16 output staging: one row of a wave tile (WN * 16 outputs) plus 16 bytes of padding
+// against LDS bank conflicts; 32 rows per wave at a time.
+template <int WN>
+constexpr int stage_row_bytes() { return WN * 32 + 16; }
+
+template <int WN, int WM, bool OUT_F32, bool GELU>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane,
+                                         uint8_t* stage) {
   if ((g.epi & SVDQ_EPI_LOWRANK) && g.r_pad > 0) {
     const int R32 = g.r_pad / 32;
     const uint4* L2f = reinterpret_cast<const uint4*>(g.wblob + g.w_L2) + (n0 / 16) * R32 * 64 + lane;
@@ -58,35 +82,66 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
       }
     }
   }
+  // bias of the lane's 4 consecutive outputs in each of the WN blocks (zero without BIAS)
+  float bv[WN][4];
   const uint16_t* bias = reinterpret_cast<const uint16_t*>(g.wblob + g.w_bias);
   const bool use_bias = (g.epi & SVDQ_EPI_BIAS) != 0;
-  const bool use_gelu = (g.epi & SVDQ_EPI_GELU) != 0;
 #pragma unroll
   for (int i = 0; i < WN; ++i) {
-    const int64_t n = n0 + i * 16 + (lane >> 4) * 4;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (use_bias) {
-      const uint2 braw = *reinterpret_cast<const uint2*>(bias + n);
-      bv[0] = bf_lo(braw.x); bv[1] = bf_hi(braw.x); bv[2] = bf_lo(braw.y); bv[3] = bf_hi(braw.y);
-    }
+    uint2 braw = make_uint2(0u, 0u);
+    if (use_bias) braw = *reinterpret_cast<const uint2*>(bias + n0 + i * 16 + (lane >> 4) * 4);
+    bv[i][0] = bf_lo(braw.x); bv[i][1] = bf_hi(braw.x); bv[i][2] = bf_lo(braw.y); bv[i][3] = bf_hi(braw.y);
+  }
+  if constexpr (OUT_F32) {
+    const bool full = (m0 + WM * 16 <= g.M) && (n0 + WN * 16 <= g.N);
 #pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      const int64_t m = m0 + j * 16 + (lane & 15);
-      if (m < g.M && n < g.N) {
+    for (int i = 0; i < WN; ++i) {
+      const int64_t n = n0 + i * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        const int64_t m = m0 + j * 16 + (lane & 15);
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          y[e] = acc[i][j][e] + bv[e];
-          if (use_gelu) y[e] = gelu_erf(y[e]);
+          y[e] = acc[i][j][e] + bv[i][e];
+          if (GELU) y[e] = gelu_erf(y[e]);
         }
-        if (OUT_F32) {
+        if (full || (m < g.M && n < g.N))
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.Y) + m * g.ldy + n) = make_float4(y[0], y[1], y[2], y[3]);
-        } else {
-          uint2 o;
-          o.x = pack_bf2(y[0], y[1]);
-          o.y = pack_bf2(y[2], y[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.Y) + m * g.ldy + n) = o;
+      }
+    }
+  } else {
+    // bf16: each pair of 16-row blocks goes through the wave's LDS staging area so
+    // that every store instruction writes whole 256-byte row segments.
+    constexpr int RB = stage_row_bytes<WN>();
+    constexpr int LPR = WN * 2;          // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;        // rows per store instruction
+    static_assert(WM % 2 == 0 && 32 % RPI == 0, "wave tile shape");
+#pragma unroll
+    for (int jp = 0; jp < WM / 2; ++jp) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * jp + jj;
+        uint8_t* row = stage + (jj * 16 + (lane & 15)) * RB + (lane >> 4) * 8;
+#pragma unroll
+        for (int i = 0; i < WN; ++i) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = acc[i][j][e] + bv[i][e];
+            if (GELU) y[e] = gelu_erf(y[e]);
+          }
+          *reinterpret_cast<uint2*>(row + i * 32) = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
         }
+      }
+#pragma unroll
+      for (int r = 0; r < 32 / RPI; ++r) {
+        const int rr = r * RPI + lane / LPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * RB + (lane % LPR) * 16);
+        const int64_t m = m0 + jp * 32 + rr;
+        const int64_t n = n0 + (lane % LPR) * 8;
+        if (m < g.M && n < g.N)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.Y) + m * g.ldy + n) = v;
       }
     }
   }
@@ -147,10 +202,13 @@ __device__ __forceinline__ void fp4_mma_stage(v4f (&acc)[WN][WM], const uint4* A
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int WN, int WM, bool OUT_F32>
+template <int WN, int WM, bool OUT_F32, bool GELU>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
-  __shared__ uint4 la0[kStageFrags * 64], la1[kStageFrags * 64];
-  __shared__ uint4 lb0[kStageFrags * 64], lb1[kStageFrags * 64];
+  __shared__ uint4 lds[4 * kStageFrags * 64];     // 64 KiB: two stages of both operands
+  uint4* const la0 = lds;
+  uint4* const la1 = lds + kStageFrags * 64;
+  uint4* const lb0 = lds + 2 * kStageFrags * 64;
+  uint4* const lb1 = lds + 3 * kStageFrags * 64;
   static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,7 +305,9 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
 #undef SVDQ_FP4_STEP
   const int64_t n0 = (nt0 + wn * WN) * 16;
   const int64_t m0 = (mt0 + wm * WM) * 16;
-  epilogue<WN, WM, OUT_F32>(g, acc, n0, m0, lane);
+  // the last step ended with a barrier, so the LDS ring is free for the output staging
+  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane,
+                                  reinterpret_cast<uint8_t*>(lds) + w * 32 * stage_row_bytes<WN>());
 }
 
 // ------------------------------------------------------------------ INT4
@@ -264,7 +324,7 @@ __device__ __forceinline__ void unpack_frag(const uint4& q, v4i& g0, v4i& g1) {
   g1 = v4i{e0, o0, e1, o1};
 }
 
-template <int WN, int WM, bool OUT_F32>
+template <int WN, int WM, bool OUT_F32, bool GELU>
 __global__ void __launch_bounds__(256) gemm_int4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
@@ -321,7 +381,8 @@ __global__ void __launch_bounds__(256) gemm_int4_kernel(GemmArgs g) {
         }
       }
   }
-  epilogue<WN, WM, OUT_F32>(g, acc, n0, m0, lane);
+  __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];
+  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
 }
 
 // ------------------------------------------------------------------ launcher
@@ -338,20 +399,22 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
   g.epi = epi;
   g.Y = Y;
   const bool f32 = (epi & SVDQ_EPI_OUT_F32) != 0;
+  const bool gelu = (epi & SVDQ_EPI_GELU) != 0;
+#define SVDQ_LAUNCH(KERNEL, WN, WM, THREADS, NB)                                                           \
+  do {                                                                                                     \
+    if (f32 && gelu) hipLaunchKernelGGL((KERNEL<WN, WM, true, true>), dim3(NB), dim3(THREADS), 0, s, g);    \
+    else if (f32) hipLaunchKernelGGL((KERNEL<WN, WM, true, false>), dim3(NB), dim3(THREADS), 0, s, g);      \
+    else if (gelu) hipLaunchKernelGGL((KERNEL<WN, WM, false, true>), dim3(NB), dim3(THREADS), 0, s, g);     \
+    else hipLaunchKernelGGL((KERNEL<WN, WM, false, false>), dim3(NB), dim3(THREADS), 0, s, g);              \
+  } while (0)
   if (fmt == kFmtMXFP4) {
     const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-    if (f32)
-      hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true>), dim3(nb), dim3(256), 0, s, g);
-    else
-      hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false>), dim3(nb), dim3(256), 0, s, g);
+    SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, nb);
   } else {
-    constexpr int WN = 4, WM = 4;
-    const unsigned nb = unsigned((wl.N_pad / (2 * WN * 16)) * (al.M_pad / (2 * WM * 16)));
-    if (f32)
-      hipLaunchKernelGGL((gemm_int4_kernel<WN, WM, true>), dim3(nb), dim3(256), 0, s, g);
-    else
-      hipLaunchKernelGGL((gemm_int4_kernel<WN, WM, false>), dim3(nb), dim3(256), 0, s, g);
+    const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
+    SVDQ_LAUNCH(gemm_int4_kernel, 4, 4, 256, nb);
   }
+#undef SVDQ_LAUNCH
   return hipGetLastError();
 }
 
