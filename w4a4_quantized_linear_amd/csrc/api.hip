@@ -9,9 +9,11 @@
 #include "layout.h"
 
 namespace svdq {
-hipError_t launch_quantize(int fmt, bool act, const void* src, int64_t rows, int64_t ld, int K, const float* lam,
-                           const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad, uint16_t* Dout,
-                           int r_pad, hipStream_t s);
+hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
+                                  uint8_t* scales, int64_t rows_pad, hipStream_t s);
+hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
+                               const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
+                               uint16_t* Dout, float* part, int r_pad, int nw, int splits, hipStream_t s);
 hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* lam, const uint16_t* bias, int K,
                            int N, int rank, const WeightLayout& wl, uint8_t* blob, hipStream_t s);
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
@@ -140,8 +142,7 @@ svdq_status svdq_pack_weight(const svdq_layer_desc* d, const float* R, const uin
   const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
   uint8_t* blob = static_cast<uint8_t*>(w_packed);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_quantize(d->fmt, false, R, d->N, d->K, d->K, nullptr, nullptr, blob + wl.codes,
-                                 blob + wl.scales, wl.N_pad, nullptr, 0, st);
+  hipError_t e = launch_quantize_weight(d->fmt, R, d->N, d->K, d->K, blob + wl.codes, blob + wl.scales, wl.N_pad, st);
   if (e != hipSuccess) return SVDQ_ERR_LAUNCH;
   return launched(launch_pack_aux(L1, L2, lambda, bias, d->K, d->N, d->rank, wl, blob, st));
 }
@@ -156,10 +157,11 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* d, const void* w_packed, co
   const ActLayout al = act_layout(d->K, d->rank, M);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
   uint8_t* ws = static_cast<uint8_t*>(a_packed);
-  return launched(launch_quantize(d->fmt, true, X, M, ldx, d->K, reinterpret_cast<const float*>(blob + wl.lam),
-                                  blob + wl.L1, ws + al.codes, ws + al.scales, al.M_pad,
-                                  reinterpret_cast<uint16_t*>(ws + al.D), int(al.r_pad),
-                                  static_cast<hipStream_t>(stream)));
+  return launched(launch_quantize_act(d->fmt, X, M, ldx, d->K, reinterpret_cast<const float*>(blob + wl.lam),
+                                      reinterpret_cast<const float*>(blob + wl.rlam), blob + wl.L1, ws + al.codes,
+                                      ws + al.scales, al.M_pad, reinterpret_cast<uint16_t*>(ws + al.D),
+                                      reinterpret_cast<float*>(ws + al.part), int(al.r_pad), al.nw, al.splits,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M, void* Y,

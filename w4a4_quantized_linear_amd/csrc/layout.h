@@ -42,7 +42,8 @@ struct WeightLayout {
 
 struct ActLayout {
   int64_t M_pad, r_pad;
-  size_t codes, scales, D, total;
+  int nw, splits;                  // activation kernel: waves per workgroup, K splits
+  size_t codes, scales, D, part, total;
 };
 
 // Codes: N_pad x K/2 bytes.  Scales: N_pad x K/32 bytes (E8M0 per 32, or fp16 per 64).
@@ -64,15 +65,40 @@ __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   return w;
 }
 
+constexpr int kActUnit = 256;      // K per wave work unit of the activation kernel
+constexpr int kActMaxWorkgroups = 4096;
+
+// Work split of the activation kernel: each workgroup takes one 16-row tile and
+// one of `splits` equal K ranges, its `nw` waves striding over 256-K units of
+// that range.  Splits raise the workgroup count well past the CU count (so the
+// last wave of workgroups is small) at the cost of an fp32 partial of the down
+// projection per split, summed in fixed order by a second small kernel.
+__host__ __device__ inline void act_split(int K, int64_t M_pad, int* nw, int* splits) {
+  const int units = K / kActUnit;
+  int w = 1;
+  for (int c = 4; c >= 1; --c)
+    if (units % c == 0) { w = c; break; }
+  const int per = units / w;                     // units per wave with one split
+  const int64_t tiles = M_pad / 16;
+  int s = 1;
+  for (int d = per; d >= 1; --d)                 // most splits within the workgroup budget
+    if (per % d == 0 && tiles * d <= kActMaxWorkgroups) { s = d; break; }
+  *nw = w;
+  *splits = s;
+}
+
 // Codes: M_pad x K/2.  Scales: M_pad x K/32 bytes.  D: M_pad x r_pad x {hi, lo} bf16.
+// part: fp32 partial down projections, splits x M_pad x r_pad (only with splits > 1).
 __host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
   ActLayout a;
   a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
   a.r_pad = round_up(rank, kRankAlign);
+  act_split(K, a.M_pad, &a.nw, &a.splits);
   size_t o = 0;
   a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
   a.scales = o; o = align256(o + size_t(a.M_pad) * K / 32);
   a.D = o;      o = align256(o + size_t(a.M_pad) * a.r_pad * 4);
+  a.part = o;   o = align256(o + (a.splits > 1 ? size_t(a.splits) * a.M_pad * a.r_pad * 4 : 0));
   a.total = o;
   return a;
 }

@@ -1,30 +1,26 @@
-// Launch 1 of the layer and the weight packer.
+// Launch 1 of the layer (quantize_act_kernel) and the weight packer.
 //
-// quantize_rows: one pass over a 16-row tile of X (activations, bf16) or R
-// (weights, fp32).  For activations it divides by lambda (the smoothing step of
-// section 4.2 of the SVDQuant notes page), and in the same pass computes the
-// down projection D = X_hat L1 on bf16 MFMA (section 4.3: the down projection is
-// fused into the quantization kernel).  Per group of g elements along K it takes
-// amax, the scale and the 4-bit codes (section 3's max-scaled quantizer; MXFP4:
-// E8M0 power of two with e = floor(log2 amax) - 2; INT4: fp16(amax / 7)), and
-// writes codes and scales straight into the GEMM's fragment layout.
-//
-// Work split: workgroup = one 16-row tile; its NW waves stride over the K/512
-// superchunks; lane (row = lane % 16, c = lane / 16) holds 8 consecutive
-// elements of each 32-element block, i.e. exactly the A fragment of the bf16
-// 16x16x32 MFMA, so the down projection needs no data movement.
+// Both quantizers apply section 3's max-scaled quantizer of the SVDQuant notes
+// page per group of g elements along K (MXFP4: E8M0 power of two with
+// e = floor(log2 amax) - 2, g = 32; INT4: fp16(amax / 7), g = 64) and write the
+// codes and scales straight into the GEMM's fragment layout.  The activation
+// kernel also divides by lambda (the smoothing step of section 4.2) and computes
+// the down projection D = X_hat L1 in the same pass over X (section 4.3: the
+// down projection is fused into the quantization kernel).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
 
 namespace svdq {
 
-template <int FMT, bool ACT, int R16>
-__global__ void __launch_bounds__(512) quantize_rows_kernel(
-    const void* __restrict__ src, int64_t rows, int64_t ld, int K, const float* __restrict__ lam,
-    const uint4* __restrict__ L1f, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    int64_t rows_pad, uint16_t* __restrict__ Dout, int r_pad) {
-  extern __shared__ float dred[];  // [NW][16][r_pad] partial down projections
+// ---- weights (load time): R, fp32, one 16-row tile per workgroup ----
+//
+// Lane (row = lane % 16, c = lane / 16) holds 8 consecutive elements of each
+// 32-element block; the workgroup's NW waves stride over K/512 superchunks.
+template <int FMT>
+__global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __restrict__ src, int64_t rows,
+                                                              int64_t ld, int K, uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales, int64_t rows_pad) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -34,10 +30,6 @@ __global__ void __launch_bounds__(512) quantize_rows_kernel(
   const bool valid = m < rows;
   const int nsuper = K / kKSuper;
 
-  v4f dacc[R16 > 0 ? R16 : 1];
-#pragma unroll
-  for (int i = 0; i < (R16 > 0 ? R16 : 1); ++i) dacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
   for (int kc = w; kc < nsuper; kc += nw) {
     uint32_t sdw = 0;  // MXFP4: this lane's scale dword of the superfragment
 #pragma unroll 2
@@ -46,29 +38,14 @@ __global__ void __launch_bounds__(512) quantize_rows_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = kc * kKSuper + (2 * p + h) * 32 + c * 8;
-        if (ACT) {
-          uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-          if (valid) raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + m * ld + k);
-          const float4 l0 = *reinterpret_cast<const float4*>(lam + k);
-          const float4 l1 = *reinterpret_cast<const float4*>(lam + k + 4);
-          x[8 * h + 0] = bf_lo(raw.x) / l0.x;
-          x[8 * h + 1] = bf_hi(raw.x) / l0.y;
-          x[8 * h + 2] = bf_lo(raw.y) / l0.z;
-          x[8 * h + 3] = bf_hi(raw.y) / l0.w;
-          x[8 * h + 4] = bf_lo(raw.z) / l1.x;
-          x[8 * h + 5] = bf_hi(raw.z) / l1.y;
-          x[8 * h + 6] = bf_lo(raw.w) / l1.z;
-          x[8 * h + 7] = bf_hi(raw.w) / l1.w;
-        } else {
-          float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-          if (valid) {
-            const float* s = reinterpret_cast<const float*>(src) + m * ld + k;
-            a = *reinterpret_cast<const float4*>(s);
-            b = *reinterpret_cast<const float4*>(s + 4);
-          }
-          x[8 * h + 0] = a.x; x[8 * h + 1] = a.y; x[8 * h + 2] = a.z; x[8 * h + 3] = a.w;
-          x[8 * h + 4] = b.x; x[8 * h + 5] = b.y; x[8 * h + 6] = b.z; x[8 * h + 7] = b.w;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (valid) {
+          const float* s = src + m * ld + k;
+          a = *reinterpret_cast<const float4*>(s);
+          b = *reinterpret_cast<const float4*>(s + 4);
         }
+        x[8 * h + 0] = a.x; x[8 * h + 1] = a.y; x[8 * h + 2] = a.z; x[8 * h + 3] = a.w;
+        x[8 * h + 4] = b.x; x[8 * h + 5] = b.y; x[8 * h + 6] = b.z; x[8 * h + 7] = b.w;
       }
 
       if (FMT == kFmtMXFP4) {
@@ -121,38 +98,225 @@ __global__ void __launch_bounds__(512) quantize_rows_kernel(
           *reinterpret_cast<_Float16*>(scales + i4_scale_byte(m, g, rows_pad)) = h16;
         }
       }
-
-      if (ACT && R16 > 0) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int jb = 2 * p + h;
-          uint4 hi, lo;
-          float r[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = x[8 * h + e] - bf_lo(f2bf(x[8 * h + e]));
-          hi.x = pack_bf2(x[8 * h + 0], x[8 * h + 1]);
-          hi.y = pack_bf2(x[8 * h + 2], x[8 * h + 3]);
-          hi.z = pack_bf2(x[8 * h + 4], x[8 * h + 5]);
-          hi.w = pack_bf2(x[8 * h + 6], x[8 * h + 7]);
-          lo.x = pack_bf2(r[0], r[1]);
-          lo.y = pack_bf2(r[2], r[3]);
-          lo.z = pack_bf2(r[4], r[5]);
-          lo.w = pack_bf2(r[6], r[7]);
-          const uint4* bf = L1f + (size_t(kc * 16 + jb) * R16) * 64 + lane;
-#pragma unroll
-          for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) {
-            const uint4 b = bf[ib * 64];
-            dacc[ib] = mfma_bf16(hi, b, dacc[ib]);
-            dacc[ib] = mfma_bf16(lo, b, dacc[ib]);
-          }
-        }
-      }
     }
     if (FMT == kFmtMXFP4)
       *reinterpret_cast<uint32_t*>(scales + (size_t(rt) * nsuper + kc) * 256 + lane * 4) = sdw;
   }
+}
 
-  if (ACT && R16 > 0) {
+// ---- launch 1 for activations ----
+//
+// Workgroup = one 16-row tile; its waves stride over 256-K units of K, and the
+// waves' partial down projections are summed in LDS at the end (fixed order).
+// Lane (row = lane % 16, c = lane / 16) holds 8 consecutive elements of each
+// 32-element block: the A fragment of the bf16 16x16x32 MFMA, so the down
+// projection needs no data movement.  Within a unit the X loads run one 64-K step
+// ahead of the math; the smoothing divide is the refined reciprocal division
+// (same result as the IEEE division, far fewer operations); the group maximum
+// over the 4 lanes of a row uses the VALU lane swaps.
+
+__device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
+  a[0] = bf_lo(r.x); a[1] = bf_hi(r.x); a[2] = bf_lo(r.y); a[3] = bf_hi(r.y);
+  a[4] = bf_lo(r.z); a[5] = bf_hi(r.z); a[6] = bf_lo(r.w); a[7] = bf_hi(r.w);
+}
+
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one row's group)
+__device__ __forceinline__ float rowgroup_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const uint32_t ua = __float_as_uint(a);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(ua, ua, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// Register budget by down-projection width: waves per SIMD the compiler must
+// leave room for (the L1 fragments and accumulators grow with the rank).
+__host__ __device__ constexpr int act_min_waves(int r16) { return r16 <= 2 ? 4 : (r16 <= 8 ? 2 : 1); }
+
+// Grid: (16-row tiles, K splits); block: nw waves (nw <= 4).  With one split
+// the workgroup writes D; otherwise it writes its fp32 partial to `part` and
+// reduce_down_kernel sums the splits.
+template <int FMT, int R16>
+__global__ void __launch_bounds__(256, act_min_waves(R16)) quantize_act_kernel(
+    const uint16_t* __restrict__ X, int64_t rows, int64_t ld, int K, const float* __restrict__ lam,
+    const float* __restrict__ rlam, const uint4* __restrict__ L1f, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t rows_pad, uint16_t* __restrict__ Dout, float* __restrict__ part,
+    int r_pad) {
+  extern __shared__ float dred[];  // [NW][16][r_pad] partial down projections
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int row = lane & 15, c = lane >> 4;
+  const int64_t rt = blockIdx.x;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int64_t m = rt * 16 + row;
+  const bool valid = m < rows;
+  const int nsuper = K / kKSuper;
+  const int per_split = (K / kActUnit) / nsplit;
+  const int u_beg = split * per_split, u_end = u_beg + per_split;
+  // Rows past the end read the last row (so no load is conditional, which
+  // keeps the compiler's wait counts exact) and use zeros instead.
+  const uint16_t* xr = X + (valid ? m : rows - 1) * ld + c * 8;
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+
+  v4f dacc[R16 > 0 ? R16 : 1];
+#pragma unroll
+  for (int i = 0; i < (R16 > 0 ? R16 : 1); ++i) dacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 cur0 = *reinterpret_cast<const uint4*>(xr + (u_beg + w) * kActUnit);
+  uint4 cur1 = *reinterpret_cast<const uint4*>(xr + (u_beg + w) * kActUnit + 32);
+  for (int u = u_beg + w; u < u_end; u += nw) {
+    const int k0 = u * kActUnit;
+    // First K of the wave's next unit (the last unit again when there is none:
+    // an in-bounds load whose value is never used).
+    const int kn = (u + nw < u_end ? u + nw : u_end - 1) * kActUnit;
+    if (!valid) cur0 = cur1 = zero4;
+    uint32_t sw = 0;  // MXFP4: this lane's two scale bytes of the unit
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {  // 64-element steps of the unit
+      // This step's lambda, 1/lambda and L1 fragments first, then the next
+      // step's X: loads complete in issue order, so waiting for the small
+      // cached loads never waits for the X prefetch behind them.
+      float4 lq[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + (2 * p + h) * 32 + c * 8;
+        lq[h][0] = *reinterpret_cast<const float4*>(lam + k);
+        lq[h][1] = *reinterpret_cast<const float4*>(lam + k + 4);
+        lq[h][2] = *reinterpret_cast<const float4*>(rlam + k);
+        lq[h][3] = *reinterpret_cast<const float4*>(rlam + k + 4);
+      }
+      uint4 l1b[2][R16 > 0 ? R16 : 1];
+      if (R16 > 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4* bf = L1f + (size_t(u * 8 + 2 * p + h) * R16) * 64 + lane;
+#pragma unroll
+          for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) l1b[h][ib] = bf[ib * 64];
+        }
+      }
+      uint4 nxt0 = make_uint4(0u, 0u, 0u, 0u), nxt1 = nxt0;
+      float x[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float lv[8] = {lq[h][0].x, lq[h][0].y, lq[h][0].z, lq[h][0].w,
+                             lq[h][1].x, lq[h][1].y, lq[h][1].z, lq[h][1].w};
+        const float rv[8] = {lq[h][2].x, lq[h][2].y, lq[h][2].z, lq[h][2].w,
+                             lq[h][3].x, lq[h][3].y, lq[h][3].z, lq[h][3].w};
+        float a[8];
+        unpack_bf8(h == 0 ? cur0 : cur1, a);
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[8 * h + e] = div_refined(a[e], lv[e], rv[e]);
+          ok = ok && div_refined_ok(a[e], x[8 * h + e]);
+        }
+        if (!ok) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[8 * h + e] = a[e] / lv[e];
+        }
+        if (h == 0) {
+          // The next step's X goes out once the first half no longer needs
+          // its registers.
+          __builtin_amdgcn_sched_barrier(0);
+          const int kx = p < 3 ? k0 + (2 * p + 2) * 32 : kn;
+          nxt0 = *reinterpret_cast<const uint4*>(xr + kx);
+          nxt1 = *reinterpret_cast<const uint4*>(xr + kx + 32);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      if (FMT == kFmtMXFP4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int jb = 2 * p + h;                 // block within the unit
+          float amax = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+          amax = rowgroup_max(amax);
+          const uint32_t sb = e8m0_of_amax(amax);
+          const float inv = inv_scale_of_e8m0(sb);
+          uint32_t cw = 0;
+          cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
+          cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
+          cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
+          cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+          const int ks = u * 2 + jb / 4;            // 128-K step
+          *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (jb & 3) * 16 + row) + c * 4) = cw;
+          if ((jb & 3) == c) sw |= sb << (8 * (jb >> 2));
+        }
+      } else {
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = rowgroup_max(amax);
+        const float s32 = amax / 7.0f;
+        const _Float16 h16 = (_Float16)fminf(s32, 65504.0f);
+        const float sc = (float)h16;
+        const float rs = 1.0f / sc;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float t[8];
+          bool ok = true;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            t[e] = div_refined(x[8 * h + e], sc, rs);
+            ok = ok && div_refined_ok(x[8 * h + e], t[e]);
+          }
+          if (!ok) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = x[8 * h + e] / sc;
+          }
+          uint32_t cw = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float tq = __builtin_rintf(fminf(fmaxf(t[e], -8.0f), 7.0f));
+            const int q = (sc == 0.0f) ? 0 : int(tq);
+            cw |= (uint32_t(q) & 0xFu) << (4 * e);
+          }
+          const int jb = 2 * p + h;
+          const int kk = (jb & 3) * 32 + c * 8;    // offset inside the 128-K step
+          const int gi = kk / 64, o = kk % 64;
+          const int ks = u * 2 + jb / 4;
+          *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (o / 16) * 16 + row) + gi * 8 + (o % 16) / 2) = cw;
+        }
+        if (c == 0) {
+          const int g = u * 4 + p;
+          *reinterpret_cast<_Float16*>(scales + i4_scale_byte(m, g, rows_pad)) = h16;
+        }
+      }
+
+      if (R16 > 0) {
+        // Down projection: x_hat as a bf16 hi + lo pair (about 16 significant
+        // bits) against the bf16 L1, accumulated in fp32.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint4 hi, lo;
+          hi.x = cvt_bf2(x[8 * h + 0], x[8 * h + 1]);
+          hi.y = cvt_bf2(x[8 * h + 2], x[8 * h + 3]);
+          hi.z = cvt_bf2(x[8 * h + 4], x[8 * h + 5]);
+          hi.w = cvt_bf2(x[8 * h + 6], x[8 * h + 7]);
+          lo.x = cvt_bf2(x[8 * h + 0] - bf_lo(hi.x), x[8 * h + 1] - bf_hi(hi.x));
+          lo.y = cvt_bf2(x[8 * h + 2] - bf_lo(hi.y), x[8 * h + 3] - bf_hi(hi.y));
+          lo.z = cvt_bf2(x[8 * h + 4] - bf_lo(hi.z), x[8 * h + 5] - bf_hi(hi.z));
+          lo.w = cvt_bf2(x[8 * h + 6] - bf_lo(hi.w), x[8 * h + 7] - bf_hi(hi.w));
+#pragma unroll
+          for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) {
+            dacc[ib] = mfma_bf16(hi, l1b[h][ib], dacc[ib]);
+            dacc[ib] = mfma_bf16(lo, l1b[h][ib], dacc[ib]);
+          }
+        }
+      }
+      cur0 = valid ? nxt0 : zero4;
+      cur1 = valid ? nxt1 : zero4;
+    }
+    if (FMT == kFmtMXFP4)
+      *reinterpret_cast<uint16_t*>(scales + (size_t(rt) * nsuper + u / 2) * 256 + lane * 4 + (u & 1) * 2) =
+          uint16_t(sw);
+  }
+
+  if (R16 > 0) {
     // Reduce the waves' partial sums in a fixed order (deterministic), then store
     // D as bf16 hi + lo in the up projection's B-fragment layout.
 #pragma unroll
@@ -164,13 +328,34 @@ __global__ void __launch_bounds__(512) quantize_rows_kernel(
       const int rr = idx / r_pad, col = idx % r_pad;
       float s = 0.f;
       for (int ww = 0; ww < nw; ++ww) s += dred[(ww * 16 + rr) * r_pad + col];
-      const uint32_t hb = f2bf(s);
-      const uint32_t lb = f2bf(s - bf_lo(hb));
-      const int64_t mm = rt * 16 + rr;
-      Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
-      Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+      if (nsplit > 1) {
+        part[((size_t(split) * rows_pad) + rt * 16) * r_pad + idx] = s;
+      } else {
+        const uint32_t hb = f2bf(s);
+        const uint32_t lb = f2bf(s - bf_lo(hb));
+        const int64_t mm = rt * 16 + rr;
+        Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
+        Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+      }
     }
   }
+}
+
+// Sum of the K splits' partial down projections, in split order, stored as
+// the bf16 hi + lo pair the GEMM epilogue reads.
+__global__ void reduce_down_kernel(const float* __restrict__ part, int splits, int64_t rows_pad, int r_pad,
+                                   uint16_t* __restrict__ Dout) {
+  const int64_t total = rows_pad * r_pad;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  float s = 0.f;
+  for (int sp = 0; sp < splits; ++sp) s += part[size_t(sp) * total + i];
+  const uint32_t hb = f2bf(s);
+  const uint32_t lb = f2bf(s - bf_lo(hb));
+  const int64_t mm = i / r_pad;
+  const int col = int(i % r_pad);
+  Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
+  Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
 }
 
 // ---- packing of the small operands (load time) ----
@@ -275,45 +460,57 @@ static int pick_waves(int K) {
   return n < 8 ? n : 8;
 }
 
-template <int FMT, bool ACT>
-static hipError_t launch_quantize_fmt(const void* src, int64_t rows, int64_t ld, int K, const float* lam,
-                                      const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
-                                      uint16_t* Dout, int r_pad, hipStream_t s) {
-  const int nw = pick_waves(K);
-  const dim3 grid(unsigned(rows_pad / 16)), block(unsigned(64 * nw));
-  const size_t shm = ACT ? size_t(nw) * 16 * r_pad * 4 : 0;
+template <int FMT>
+static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
+                                          const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales,
+                                          int64_t rows_pad, uint16_t* Dout, float* part, int r_pad, int nw,
+                                          int splits, hipStream_t s) {
+  const dim3 grid(unsigned(rows_pad / 16), unsigned(splits)), block(unsigned(64 * nw));
+  const size_t shm = size_t(nw) * 16 * r_pad * 4;
   const uint4* l1 = reinterpret_cast<const uint4*>(L1f);
-#define SVDQ_Q(R16)                                                                                         \
-  hipLaunchKernelGGL((quantize_rows_kernel<FMT, ACT, R16>), grid, block, shm, s, src, rows, ld, K, lam, l1, \
-                     codes, scales, rows_pad, Dout, r_pad)
-  if constexpr (!ACT) {
-    SVDQ_Q(0);
-  } else {
-    switch (r_pad / 16) {
-      case 0: SVDQ_Q(0); break;
-      case 2: SVDQ_Q(2); break;
-      case 4: SVDQ_Q(4); break;
-      case 6: SVDQ_Q(6); break;
-      case 8: SVDQ_Q(8); break;
-      case 10: SVDQ_Q(10); break;
-      case 12: SVDQ_Q(12); break;
-      case 14: SVDQ_Q(14); break;
-      case 16: SVDQ_Q(16); break;
-      default: return hipErrorInvalidValue;
-    }
+#define SVDQ_QA(R16)                                                                                      \
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, R16>), grid, block, shm, s, X, rows, ld, K, lam, rlam, l1, \
+                     codes, scales, rows_pad, Dout, part, r_pad)
+  switch (r_pad / 16) {
+    case 0: SVDQ_QA(0); break;
+    case 2: SVDQ_QA(2); break;
+    case 4: SVDQ_QA(4); break;
+    case 6: SVDQ_QA(6); break;
+    case 8: SVDQ_QA(8); break;
+    case 10: SVDQ_QA(10); break;
+    case 12: SVDQ_QA(12); break;
+    case 14: SVDQ_QA(14); break;
+    case 16: SVDQ_QA(16); break;
+    default: return hipErrorInvalidValue;
   }
-#undef SVDQ_Q
+#undef SVDQ_QA
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1 || r_pad == 0) return e;
+  const int64_t total = rows_pad * r_pad;
+  hipLaunchKernelGGL(reduce_down_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, part, splits,
+                     rows_pad, r_pad, Dout);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(int fmt, bool act, const void* src, int64_t rows, int64_t ld, int K, const float* lam,
-                           const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad, uint16_t* Dout,
-                           int r_pad, hipStream_t s) {
+hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
+                               const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
+                               uint16_t* Dout, float* part, int r_pad, int nw, int splits, hipStream_t s) {
   if (fmt == kFmtMXFP4)
-    return act ? launch_quantize_fmt<kFmtMXFP4, true>(src, rows, ld, K, lam, L1f, codes, scales, rows_pad, Dout, r_pad, s)
-               : launch_quantize_fmt<kFmtMXFP4, false>(src, rows, ld, K, lam, L1f, codes, scales, rows_pad, Dout, r_pad, s);
-  return act ? launch_quantize_fmt<kFmtINT4, true>(src, rows, ld, K, lam, L1f, codes, scales, rows_pad, Dout, r_pad, s)
-             : launch_quantize_fmt<kFmtINT4, false>(src, rows, ld, K, lam, L1f, codes, scales, rows_pad, Dout, r_pad, s);
+    return launch_quantize_act_fmt<kFmtMXFP4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
+                                              r_pad, nw, splits, s);
+  return launch_quantize_act_fmt<kFmtINT4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
+                                           r_pad, nw, splits, s);
+}
+
+hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
+                                  uint8_t* scales, int64_t rows_pad, hipStream_t s) {
+  const int nw = pick_waves(K);
+  const dim3 grid(unsigned(rows_pad / 16)), block(unsigned(64 * nw));
+  if (fmt == kFmtMXFP4)
+    hipLaunchKernelGGL((quantize_weight_kernel<kFmtMXFP4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad);
+  else
+    hipLaunchKernelGGL((quantize_weight_kernel<kFmtINT4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad);
+  return hipGetLastError();
 }
 
 static unsigned grid_for(int64_t total, int block) {
