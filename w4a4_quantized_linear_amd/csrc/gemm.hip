@@ -151,20 +151,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 //
 // 256 threads = 4 waves (1 per SIMD, so each has the full register file), workgroup
 // tile 256 (n) x 256 (m), wave tile 128 (n) x 128 (m) = 8 x 8 MFMA blocks with the
-// accumulators in AGPRs.  Per 128-K step a stage holds 16 weight and 16 activation
-// fragments (32 KiB); each wave fetches 8 of them with buffer loads two steps
-// ahead into one of two register staging sets, writes them to one of two LDS
-// buffers one step ahead, and computes from the other.  The E8M0 scales of a
-// 512-K superfragment (one dword per lane and 16-row tile) are loaded into
-// registers one superfragment ahead; the MFMA of step u of the superfragment
-// picks byte u of the dword.
-//
-// Step t (buffer t % 2):  issue loads of step t+2 into staging set t % 2;
-// compute step t from LDS buffer t % 2; write staging set (t+1) % 2 (step t+1)
-// into LDS buffer (t+1) % 2; wait for the LDS writes; barrier.  The barrier uses
-// no memory fence, which would also wait for the loads still in flight.
+// accumulators in AGPRs.  A stage (one 128-K step) is 16 weight and 16 activation
+// fragments, 32 KiB; LDS holds a ring of three stages.  In step t a wave
+//   - writes its share of stage t+2 (fetched into registers during step t-1)
+//     into ring slot (t+2) % 3,
+//   - fetches its share of stage t+3 from global memory (buffer loads),
+//   - runs the 64 MFMAs of stage t from registers, reading each of its 16
+//     fragments of stage t+1 from slot (t+1) % 3 into the register that the
+//     finished MFMAs no longer need,
+// with the LDS and memory operations interleaved between the MFMAs, and ends
+// with one barrier.  Slot (t+2) % 3 last held stage t-1, whose reads finished
+// before the barrier of step t-2, and slot (t+1) % 3 was written before the
+// barrier of step t-1, so one barrier per step orders everything.  The E8M0
+// scales of a 512-K superfragment (one dword per lane and 16-row tile) are
+// loaded one superfragment ahead; the MFMA of step u of the superfragment picks
+// byte u of the dword.
 
 constexpr int kStageFrags = 16;                 // fragments per operand per stage
+constexpr int kRing = 3;                        // LDS stages
+constexpr int kStageU4 = 2 * kStageFrags * 64;  // uint4 per stage (weights, then activations)
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
 
 // Buffer resource over [base, base + bytes): loads beyond the end return zero.
@@ -178,37 +183,18 @@ __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t vo
 }
 
 // Wait for this wave's LDS operations, then a workgroup barrier without a memory
-// fence; the empty asm keeps the compiler from moving LDS accesses across it.
+// fence (a fence would also wait for the global loads still in flight); the
+// empty asm keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x0 << 8) | 0xF | (0x3 << 14));   // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-template <int U, int WN, int WM>
-__device__ __forceinline__ void fp4_mma_stage(v4f (&acc)[WN][WM], const uint4* A, const uint4* B,
-                                              const uint32_t (&sa)[WN], const uint32_t (&sb)[WM], int lane) {
-  // all fragment reads first, so their latency overlaps the first MFMAs
-  uint4 af[WN], bf[WM];
-#pragma unroll
-  for (int j = 0; j < WM; ++j) bf[j] = B[j * 64 + lane];
-#pragma unroll
-  for (int i = 0; i < WN; ++i) af[i] = A[i * 64 + lane];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < WN; ++i)
-#pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = mfma_fp4_sel<U>(af[i], bf[j], acc[i][j], sa[i], sb[j]);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 template <int WN, int WM, bool OUT_F32, bool GELU>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
-  __shared__ uint4 lds[4 * kStageFrags * 64];     // 64 KiB: two stages of both operands
-  uint4* const la0 = lds;
-  uint4* const la1 = lds + kStageFrags * 64;
-  uint4* const lb0 = lds + 2 * kStageFrags * 64;
-  uint4* const lb1 = lds + 3 * kStageFrags * 64;
+  __shared__ uint4 lds[kRing * kStageU4];         // 96 KiB
   static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -228,8 +214,6 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rSA = make_rsrc(g.wblob + g.w_scales + size_t(nt0) * KSUP * 256, scale_bytes);
   const __amdgpu_buffer_rsrc_t rSB = make_rsrc(g.act + g.a_scales + size_t(mt0) * KSUP * 256, scale_bytes);
   const uint32_t voff16 = uint32_t(lane) * 16, voff4 = uint32_t(lane) * 4;
-  uint4* const la[2] = {la0, la1};
-  uint4* const lb[2] = {lb0, lb1};
 
   v4f acc[WN][WM];
 #pragma unroll
@@ -247,49 +231,76 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
     for (int j = 0; j < WM; ++j)
       y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WM + j) * KSUP + sup) * 256, 0);
   };
-  // this wave's share of a stage: fragments 4w .. 4w+3 of each operand
-  uint4 stA[2][4], stB[2][4];
-  auto fetch = [&](int step, uint4 (&xa)[4], uint4 (&xb)[4]) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint32_t so = uint32_t((4 * w + f) * KS + step) * 1024;
-      xa[f] = load_frag(rA, voff16, so);
-      xb[f] = load_frag(rB, voff16, so);
-    }
+  // this wave's share of a stage: weight fragments 4w .. 4w+3 (st[0..3]) and
+  // activation fragments 4w .. 4w+3 (st[4..7])
+  uint4 st[8];
+  auto fetch1 = [&](int step, int f) {
+    const uint32_t so = uint32_t((4 * w + (f & 3)) * KS + step) * 1024;
+    st[f] = load_frag(f < 4 ? rA : rB, voff16, so);
   };
-  auto stash = [&](const uint4 (&xa)[4], const uint4 (&xb)[4], int buf) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      la[buf][(4 * w + f) * 64 + lane] = xa[f];
-      lb[buf][(4 * w + f) * 64 + lane] = xb[f];
-    }
+  auto stash1 = [&](int slot, int f) {
+    lds[slot * kStageU4 + ((f < 4 ? 0 : kStageFrags) + 4 * w + (f & 3)) * 64 + lane] = st[f];
   };
+  auto frag_a = [&](int slot, int i) { return lds[slot * kStageU4 + (wn * WN + i) * 64 + lane]; };
+  auto frag_b = [&](int slot, int j) { return lds[slot * kStageU4 + (kStageFrags + wm * WM + j) * 64 + lane]; };
+  // Fragments in registers, reloaded in place: row i's weight fragment for the
+  // next step is read once row i's MFMAs are issued, and activation fragment j
+  // once the last row's MFMA j is issued (the step's closing barrier waits for
+  // these reads anyway).
+  uint4 fa[WN], fb[WM];
 
-  // prologue: scales of superfragment 0; stage 0 into LDS buffer 0; stage 1 in flight
+  // prologue: stages 0 and 1 into slots 0 and 1, stage 2 in flight, stage 0 in registers
   load_scales(sa, sb, 0);
-  fetch(0, stA[0], stB[0]);
-  fetch(1, stA[1], stB[1]);
-  stash(stA[0], stB[0], 0);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) fetch1(0, f);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) stash1(0, f);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) fetch1(1, f);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) stash1(1, f);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) fetch1(2, f);
   lds_barrier();
+#pragma unroll
+  for (int j = 0; j < WM; ++j) fb[j] = frag_b(0, j);
+#pragma unroll
+  for (int i = 0; i < WN; ++i) fa[i] = frag_a(0, i);
 
-  // Steady state: every step fetches two ahead and stashes one ahead; the last
-  // superfragment is peeled so the loop body has no branches.
-#define SVDQ_FP4_STEP(U, FETCH, STASH)                                                                \
+  // Step U of a superfragment.  Row i of the 8 x 8 MFMA block also stashes
+  // st[i] (stage step+2) into ring slot (step+2) % 3, refetches it (stage
+  // step+3) and reads the next step's fragments.  The flags drop the stash /
+  // fetch / read of stages past the end in the peeled last superfragment
+  // (peeling keeps the loop body free of branches).  The scheduling barriers
+  // keep each row's memory operations between its MFMAs and stop the scheduler
+  // from interleaving rows, which would make the register allocator move
+  // accumulators around.
+#define SVDQ_FP4_STEP(U, STASH, FETCH, READ)                                                          \
   {                                                                                                   \
-    if (FETCH) fetch(t0 + (U) + 2, stA[(U) & 1], stB[(U) & 1]);                                      \
-    if ((U) == 1 && (FETCH) && sup + 1 < KSUP) load_scales(san, sbn, sup + 1);                       \
-    __builtin_amdgcn_sched_barrier(0); /* keep the prefetch at the top of the step */                 \
-    fp4_mma_stage<(U)>(acc, la[(U) & 1] + (wn * WN) * 64, lb[(U) & 1] + (wm * WM) * 64, sa, sb, lane); \
-    if (STASH) stash(stA[((U) + 1) & 1], stB[((U) + 1) & 1], ((U) + 1) & 1);                        \
+    const int step = t0 + (U);                                                                        \
+    const int s2 = (step + 2) % kRing, s1 = (step + 1) % kRing;                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                                \
+    _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
+      if (STASH) stash1(s2, i);                                                                       \
+      if (FETCH) fetch1(step + 3, i);                                                                 \
+      _Pragma("unroll") for (int j = 0; j < WM; ++j) {                                                \
+        acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
+        if ((READ) && i == WN - 1) fb[j] = frag_b(s1, j);                                             \
+      }                                                                                               \
+      if (READ) fa[i] = frag_a(s1, i);                                                                \
+      __builtin_amdgcn_sched_barrier(0);                                                              \
+    }                                                                                                 \
+    if ((U) == 1 && (FETCH) && sup + 1 < KSUP) load_scales(san, sbn, sup + 1);                        \
+    __builtin_amdgcn_sched_barrier(0);                                                                \
     lds_barrier();                                                                                    \
   }
   int sup = 0;
   for (; sup + 1 < KSUP; ++sup) {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true)
-    SVDQ_FP4_STEP(1, true, true)
-    SVDQ_FP4_STEP(2, true, true)
-    SVDQ_FP4_STEP(3, true, true)
+    SVDQ_FP4_STEP(0, true, true, true)
+    SVDQ_FP4_STEP(1, true, true, true)
+    SVDQ_FP4_STEP(2, true, true, true)
+    SVDQ_FP4_STEP(3, true, true, true)
 #pragma unroll
     for (int i = 0; i < WN; ++i) sa[i] = san[i];
 #pragma unroll
@@ -297,10 +308,10 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   }
   {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true)
-    SVDQ_FP4_STEP(1, true, true)
-    SVDQ_FP4_STEP(2, false, true)
-    SVDQ_FP4_STEP(3, false, false)
+    SVDQ_FP4_STEP(0, true, true, true)
+    SVDQ_FP4_STEP(1, true, false, true)
+    SVDQ_FP4_STEP(2, false, false, true)
+    SVDQ_FP4_STEP(3, false, false, false)
   }
 #undef SVDQ_FP4_STEP
   const int64_t n0 = (nt0 + wn * WN) * 16;
