@@ -34,56 +34,41 @@ struct GemmArgs {
   void* Y;
 };
 
-// ------------------------------------------------------------------ epilogue
-//
-// Low-rank MFMAs first (their operand loads come before any store), then every
-// bias value the wave needs, then bias + activation + conversion + stores with no
-// loads in between: on this architecture the vector-memory counter also counts
-// stores, so a load waited on inside the store sequence would wait for the stores.
-// A wave tile entirely inside Y takes the store path without per-block checks.
-
-template <int WN, int WM, bool OUT_F32>
-__device__ __forceinline__ void store_block(const GemmArgs& g, int64_t m, int64_t n, const float (&y)[4]) {
-  if (OUT_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.Y) + m * g.ldy + n) = make_float4(y[0], y[1], y[2], y[3]);
-  } else {
-    uint2 o;
-    o.x = pack_bf2(y[0], y[1]);
-    o.y = pack_bf2(y[2], y[3]);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.Y) + m * g.ldy + n) = o;
-  }
-}
+// ------------------------------------------------------------------ epilogue pieces
 
 // bf16 output staging: one row of a wave tile (WN * 16 outputs) plus 16 bytes of padding
 // against LDS bank conflicts; 32 rows per wave at a time.
 template <int WN>
 constexpr int stage_row_bytes() { return WN * 32 + 16; }
 
-template <int WN, int WM, bool OUT_F32, bool GELU>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane,
-                                         uint8_t* stage) {
-  if ((g.epi & SVDQ_EPI_LOWRANK) && g.r_pad > 0) {
-    const int R32 = g.r_pad / 32;
-    const uint4* L2f = reinterpret_cast<const uint4*>(g.wblob + g.w_L2) + (n0 / 16) * R32 * 64 + lane;
-    const uint4* Df = reinterpret_cast<const uint4*>(g.act + g.a_D) + (m0 / 16) * R32 * 128 + lane;
-    for (int r32 = 0; r32 < R32; ++r32) {
-      uint4 l2[WN];
+// acc += (X_hat L1) L2 over the wave tile: bf16 MFMAs of L2 (A) against D hi and lo (B).
+template <int WN, int WM>
+__device__ __forceinline__ void add_lowrank(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0,
+                                            int lane) {
+  if (!(g.epi & SVDQ_EPI_LOWRANK) || g.r_pad == 0) return;
+  const int R32 = g.r_pad / 32;
+  const uint4* L2f = reinterpret_cast<const uint4*>(g.wblob + g.w_L2) + (n0 / 16) * R32 * 64 + lane;
+  const uint4* Df = reinterpret_cast<const uint4*>(g.act + g.a_D) + (m0 / 16) * R32 * 128 + lane;
+  for (int r32 = 0; r32 < R32; ++r32) {
+    uint4 l2[WN];
 #pragma unroll
-      for (int i = 0; i < WN; ++i) l2[i] = L2f[(i * R32 + r32) * 64];
+    for (int i = 0; i < WN; ++i) l2[i] = L2f[(i * R32 + r32) * 64];
 #pragma unroll
-      for (int j = 0; j < WM; ++j) {
-        const uint4 dh = Df[(j * R32 + r32) * 128];
-        const uint4 dl = Df[(j * R32 + r32) * 128 + 64];
+    for (int j = 0; j < WM; ++j) {
+      const uint4 dh = Df[(j * R32 + r32) * 128];
+      const uint4 dl = Df[(j * R32 + r32) * 128 + 64];
 #pragma unroll
-        for (int i = 0; i < WN; ++i) {
-          acc[i][j] = mfma_bf16(l2[i], dh, acc[i][j]);
-          acc[i][j] = mfma_bf16(l2[i], dl, acc[i][j]);
-        }
+      for (int i = 0; i < WN; ++i) {
+        acc[i][j] = mfma_bf16(l2[i], dh, acc[i][j]);
+        acc[i][j] = mfma_bf16(l2[i], dl, acc[i][j]);
       }
     }
   }
-  // bias of the lane's 4 consecutive outputs in each of the WN blocks (zero without BIAS)
-  float bv[WN][4];
+}
+
+// Bias of the lane's 4 consecutive outputs in each of the WN blocks (zero without BIAS).
+template <int WN>
+__device__ __forceinline__ void load_bias(const GemmArgs& g, int64_t n0, int lane, float (&bv)[WN][4]) {
   const uint16_t* bias = reinterpret_cast<const uint16_t*>(g.wblob + g.w_bias);
   const bool use_bias = (g.epi & SVDQ_EPI_BIAS) != 0;
 #pragma unroll
@@ -92,6 +77,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
     if (use_bias) braw = *reinterpret_cast<const uint2*>(bias + n0 + i * 16 + (lane >> 4) * 4);
     bv[i][0] = bf_lo(braw.x); bv[i][1] = bf_hi(braw.x); bv[i][2] = bf_lo(braw.y); bv[i][3] = bf_hi(braw.y);
   }
+}
+
+// Y = act(acc (+ bias)) for the wave tile.  fp32 output: one 16-byte store per
+// lane and block.  bf16 output: each pair of 16-row blocks goes through the
+// wave's LDS staging area so that every store instruction writes whole
+// 256-byte row segments.
+template <int WN, int WM, bool OUT_F32, bool GELU, bool ADD_BIAS>
+__device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
+                                          int64_t n0, int64_t m0, int lane, uint8_t* stage) {
+  auto act = [&](int i, int j, float (&y)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = ADD_BIAS ? acc[i][j][e] + bv[i][e] : acc[i][j][e];
+      if (GELU) y[e] = gelu_erf(y[e]);
+    }
+  };
   if constexpr (OUT_F32) {
     const bool full = (m0 + WM * 16 <= g.M) && (n0 + WN * 16 <= g.N);
 #pragma unroll
@@ -101,18 +102,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
       for (int j = 0; j < WM; ++j) {
         const int64_t m = m0 + j * 16 + (lane & 15);
         float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = acc[i][j][e] + bv[i][e];
-          if (GELU) y[e] = gelu_erf(y[e]);
-        }
+        act(i, j, y);
         if (full || (m < g.M && n < g.N))
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.Y) + m * g.ldy + n) = make_float4(y[0], y[1], y[2], y[3]);
       }
     }
   } else {
-    // bf16: each pair of 16-row blocks goes through the wave's LDS staging area so
-    // that every store instruction writes whole 256-byte row segments.
     constexpr int RB = stage_row_bytes<WN>();
     constexpr int LPR = WN * 2;          // lanes per row (16 bytes each)
     constexpr int RPI = 64 / LPR;        // rows per store instruction
@@ -126,11 +121,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 #pragma unroll
         for (int i = 0; i < WN; ++i) {
           float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = acc[i][j][e] + bv[i][e];
-            if (GELU) y[e] = gelu_erf(y[e]);
-          }
+          act(i, j, y);
           *reinterpret_cast<uint2*>(row + i * 32) = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
         }
       }
@@ -147,28 +138,42 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
   }
 }
 
+// Whole epilogue after the main loop: low-rank MFMAs first (their operand loads
+// come before any store), then every bias value, then bias + activation +
+// conversion + stores with no loads in between (the vector-memory counter also
+// counts stores, so a load waited on among the stores would wait for them).
+template <int WN, int WM, bool OUT_F32, bool GELU>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane,
+                                         uint8_t* stage) {
+  add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+  float bv[WN][4];
+  load_bias<WN>(g, n0, lane, bv);
+  store_out<WN, WM, OUT_F32, GELU, true>(g, acc, bv, n0, m0, lane, stage);
+}
+
 // ------------------------------------------------------------------ MXFP4
 //
 // 256 threads = 4 waves (1 per SIMD, so each has the full register file), workgroup
 // tile 256 (n) x 256 (m), wave tile 128 (n) x 128 (m) = 8 x 8 MFMA blocks with the
 // accumulators in AGPRs.  A stage (one 128-K step) is 16 weight and 16 activation
-// fragments, 32 KiB; LDS holds a ring of three stages.  In step t a wave
-//   - writes its share of stage t+2 (fetched into registers during step t-1)
-//     into ring slot (t+2) % 3,
-//   - fetches its share of stage t+3 from global memory (buffer loads),
-//   - runs the 64 MFMAs of stage t from registers, reading each of its 16
-//     fragments of stage t+1 from slot (t+1) % 3 into the register that the
+// fragments, 32 KiB.  LDS holds a ring of four stages, filled by buffer loads
+// that write LDS directly (no staging registers), so a fetch has two steps to
+// land.  In step t a wave
+//   - issues its 8 fragment loads of stage t+3 into ring slot (t+3) % 4,
+//   - runs the 64 MFMAs of stage t from registers, and reads each of its 16
+//     fragments of stage t+1 from slot (t+1) % 4 into the register that the
 //     finished MFMAs no longer need,
-// with the LDS and memory operations interleaved between the MFMAs, and ends
-// with one barrier.  Slot (t+2) % 3 last held stage t-1, whose reads finished
-// before the barrier of step t-2, and slot (t+1) % 3 was written before the
-// barrier of step t-1, so one barrier per step orders everything.  The E8M0
-// scales of a 512-K superfragment (one dword per lane and 16-row tile) are
-// loaded one superfragment ahead; the MFMA of step u of the superfragment picks
-// byte u of the dword.
+//   - waits for its loads issued before this step (stage t+2) and for its LDS
+//     reads, then joins the workgroup barrier.
+// Slot (t+3) % 4 last held stage t-1, read during step t-2; slot (t+1) % 4 was
+// loaded during step t-2 and every wave waited for its share before the
+// barrier of step t-1.  Slots are separate LDS arrays indexed by compile-time
+// constants, so the compiler can tell the loads into one slot from the reads
+// of another and adds no waits of its own.  The E8M0 scales of a 512-K
+// superfragment (one dword per lane and 16-row tile) are loaded one
+// superfragment ahead; the MFMA of step u of the superfragment picks byte u.
 
 constexpr int kStageFrags = 16;                 // fragments per operand per stage
-constexpr int kRing = 3;                        // LDS stages
 constexpr int kStageU4 = 2 * kStageFrags * 64;  // uint4 per stage (weights, then activations)
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
 
@@ -182,19 +187,27 @@ __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t vo
   return make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
 }
 
-// Wait for this wave's LDS operations, then a workgroup barrier without a memory
-// fence (a fence would also wait for the global loads still in flight); the
-// empty asm keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x0 << 8) | 0xF | (0x3 << 14));   // lgkmcnt(0) only
+// One fragment (64 lanes x 16 bytes) from global memory straight into LDS at
+// `dst` (wave-uniform).
+__device__ __forceinline__ void load_frag_lds(__amdgpu_buffer_rsrc_t r, uint4* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst), 16, voff, soff, 0, 0);
+}
+
+// Wait until at most VM vector-memory operations of this wave are in flight and
+// its LDS operations are done, then a workgroup barrier without a memory fence
+// (a fence would wait for every load in flight); the empty asm keeps the
+// compiler from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 template <int WN, int WM, bool OUT_F32, bool GELU>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
-  __shared__ uint4 lds[kRing * kStageU4];         // 96 KiB
+  __shared__ uint4 ring0[kStageU4], ring1[kStageU4], ring2[kStageU4], ring3[kStageU4];   // 4 x 32 KiB
   static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -206,6 +219,9 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   const int64_t nt0 = int64_t(tn) * (BN / 16);    // first 16-row weight tile of the workgroup
   const int64_t mt0 = int64_t(tm) * (BM / 16);
   const int KS = g.K / kKStep, KSUP = g.K / kKSuper;
+  const int64_t n0 = (nt0 + wn * WN) * 16;
+  const int64_t m0 = (mt0 + wm * WM) * 16;
+  auto slot = [&](int u) -> uint4* { return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3; };
 
   // Per-workgroup views of the operands: 16 row tiles of codes and of scales each.
   const uint32_t code_bytes = uint32_t(kStageFrags) * KS * 1024, scale_bytes = uint32_t(kStageFrags) * KSUP * 256;
@@ -214,12 +230,6 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rSA = make_rsrc(g.wblob + g.w_scales + size_t(nt0) * KSUP * 256, scale_bytes);
   const __amdgpu_buffer_rsrc_t rSB = make_rsrc(g.act + g.a_scales + size_t(mt0) * KSUP * 256, scale_bytes);
   const uint32_t voff16 = uint32_t(lane) * 16, voff4 = uint32_t(lane) * 4;
-
-  v4f acc[WN][WM];
-#pragma unroll
-  for (int i = 0; i < WN; ++i)
-#pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // E8M0 scales of this wave's 8 weight tiles and 8 activation tiles, one superfragment
   uint32_t sa[WN], sb[WM], san[WN], sbn[WM];
@@ -231,58 +241,54 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
     for (int j = 0; j < WM; ++j)
       y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WM + j) * KSUP + sup) * 256, 0);
   };
-  // this wave's share of a stage: weight fragments 4w .. 4w+3 (st[0..3]) and
-  // activation fragments 4w .. 4w+3 (st[4..7])
-  uint4 st[8];
-  auto fetch1 = [&](int step, int f) {
+  // This wave's share of a stage: weight fragments 4w .. 4w+3 (f = 0..3) and
+  // activation fragments 4w .. 4w+3 (f = 4..7).
+  auto fetch1 = [&](uint4* dst_stage, int step, int f) {
     const uint32_t so = uint32_t((4 * w + (f & 3)) * KS + step) * 1024;
-    st[f] = load_frag(f < 4 ? rA : rB, voff16, so);
+    load_frag_lds(f < 4 ? rA : rB, dst_stage + ((f < 4 ? 0 : kStageFrags) + 4 * w + (f & 3)) * 64, voff16, so);
   };
-  auto stash1 = [&](int slot, int f) {
-    lds[slot * kStageU4 + ((f < 4 ? 0 : kStageFrags) + 4 * w + (f & 3)) * 64 + lane] = st[f];
-  };
-  auto frag_a = [&](int slot, int i) { return lds[slot * kStageU4 + (wn * WN + i) * 64 + lane]; };
-  auto frag_b = [&](int slot, int j) { return lds[slot * kStageU4 + (kStageFrags + wm * WM + j) * 64 + lane]; };
-  // Fragments in registers, reloaded in place: row i's weight fragment for the
-  // next step is read once row i's MFMAs are issued, and activation fragment j
-  // once the last row's MFMA j is issued (the step's closing barrier waits for
-  // these reads anyway).
-  uint4 fa[WN], fb[WM];
+  auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
+  auto frag_b = [&](const uint4* st, int j) { return st[(kStageFrags + wm * WM + j) * 64 + lane]; };
 
-  // prologue: stages 0 and 1 into slots 0 and 1, stage 2 in flight, stage 0 in registers
+  // Prologue: scales of superfragment 0, then stages 0..2 into slots 0..2.
+  v4f acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   load_scales(sa, sb, 0);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(0, f);
+  for (int f = 0; f < 8; ++f) fetch1(ring0, 0, f);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) stash1(0, f);
+  for (int f = 0; f < 8; ++f) fetch1(ring1, 1, f);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(1, f);
+  for (int f = 0; f < 8; ++f) fetch1(ring2, 2, f);
+  wait_barrier<8>();                               // stages 0 and 1 are in LDS
+  // Fragments in registers, reloaded in place: row i's weight fragment for the
+  // next step is read once row i's MFMAs are issued, and activation fragment j
+  // once the last row's MFMA j is issued (the step's closing wait covers them).
+  uint4 fa[WN], fb[WM];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) stash1(1, f);
+  for (int j = 0; j < WM; ++j) fb[j] = frag_b(ring0, j);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(2, f);
-  lds_barrier();
-#pragma unroll
-  for (int j = 0; j < WM; ++j) fb[j] = frag_b(0, j);
-#pragma unroll
-  for (int i = 0; i < WN; ++i) fa[i] = frag_a(0, i);
+  for (int i = 0; i < WN; ++i) fa[i] = frag_a(ring0, i);
 
-  // Step U of a superfragment.  Row i of the 8 x 8 MFMA block also stashes
-  // st[i] (stage step+2) into ring slot (step+2) % 3, refetches it (stage
-  // step+3) and reads the next step's fragments.  The flags drop the stash /
-  // fetch / read of stages past the end in the peeled last superfragment
-  // (peeling keeps the loop body free of branches).  The scheduling barriers
-  // keep each row's memory operations between its MFMAs and stop the scheduler
-  // from interleaving rows, which would make the register allocator move
-  // accumulators around.
-#define SVDQ_FP4_STEP(U, STASH, FETCH, READ)                                                          \
+  // Step U of a superfragment.  Row i of the 8 x 8 MFMA block also issues one
+  // fragment load of stage step+3 and reads the next step's fragments.  The flags
+  // drop the loads / reads of stages past the end in the peeled last
+  // superfragment (peeling keeps the loop body free of branches); VM is the
+  // number of vector-memory operations the step itself issues.  The scheduling
+  // barriers keep each row's memory operations between its MFMAs and stop the
+  // scheduler from interleaving rows, which would make the register allocator
+  // move accumulators around.
+#define SVDQ_FP4_STEP(U, FETCH, READ, SCALES, VM)                                                     \
   {                                                                                                   \
     const int step = t0 + (U);                                                                        \
-    const int s2 = (step + 2) % kRing, s1 = (step + 1) % kRing;                                       \
+    uint4* const s3 = slot(((U) + 3) & 3);                                                            \
+    const uint4* const s1 = slot(((U) + 1) & 3);                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                \
     _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
-      if (STASH) stash1(s2, i);                                                                       \
-      if (FETCH) fetch1(step + 3, i);                                                                 \
+      if (FETCH) fetch1(s3, step + 3, i);                                                             \
       _Pragma("unroll") for (int j = 0; j < WM; ++j) {                                                \
         acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
         if ((READ) && i == WN - 1) fb[j] = frag_b(s1, j);                                             \
@@ -290,17 +296,17 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
       if (READ) fa[i] = frag_a(s1, i);                                                                \
       __builtin_amdgcn_sched_barrier(0);                                                              \
     }                                                                                                 \
-    if ((U) == 1 && (FETCH) && sup + 1 < KSUP) load_scales(san, sbn, sup + 1);                        \
+    if (SCALES) load_scales(san, sbn, sup + 1);                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                \
-    lds_barrier();                                                                                    \
+    wait_barrier<(VM)>();                                                                             \
   }
   int sup = 0;
   for (; sup + 1 < KSUP; ++sup) {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, true)
-    SVDQ_FP4_STEP(1, true, true, true)
-    SVDQ_FP4_STEP(2, true, true, true)
-    SVDQ_FP4_STEP(3, true, true, true)
+    SVDQ_FP4_STEP(0, true, true, false, 8)
+    SVDQ_FP4_STEP(1, true, true, true, 8 + WN + WM)
+    SVDQ_FP4_STEP(2, true, true, false, 8)
+    SVDQ_FP4_STEP(3, true, true, false, 8)
 #pragma unroll
     for (int i = 0; i < WN; ++i) sa[i] = san[i];
 #pragma unroll
@@ -308,17 +314,15 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   }
   {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, true)
-    SVDQ_FP4_STEP(1, true, false, true)
-    SVDQ_FP4_STEP(2, false, false, true)
-    SVDQ_FP4_STEP(3, false, false, false)
+    SVDQ_FP4_STEP(0, true, true, false, 8)
+    SVDQ_FP4_STEP(1, false, true, false, 0)
+    SVDQ_FP4_STEP(2, false, true, false, 0)
+    SVDQ_FP4_STEP(3, false, false, false, 0)
   }
 #undef SVDQ_FP4_STEP
-  const int64_t n0 = (nt0 + wn * WN) * 16;
-  const int64_t m0 = (mt0 + wm * WM) * 16;
-  // the last step ended with a barrier, so the LDS ring is free for the output staging
-  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane,
-                                  reinterpret_cast<uint8_t*>(lds) + w * 32 * stage_row_bytes<WN>());
+  // every wave passed the last barrier with no load in flight: the ring is free
+  // for the output staging (one slot per wave)
+  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
 }
 
 // ------------------------------------------------------------------ INT4
