@@ -264,36 +264,45 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
 #pragma unroll
   for (int f = 0; f < 8; ++f) fetch1(ring2, 2, f);
   wait_barrier<8>();                               // stages 0 and 1 are in LDS
-  // Fragments in registers, reloaded in place: row i's weight fragment for the
-  // next step is read once row i's MFMAs are issued, and activation fragment j
-  // once the last row's MFMA j is issued (the step's closing wait covers them).
+  // Fragments in registers, reloaded in place.  A step runs its 8 x 8 MFMAs in
+  // two halves by activation fragment: half 0 uses fb[0..3] and meanwhile reads
+  // fb[4..7] of the same stage; half 1 uses fb[4..7] and meanwhile reads the
+  // next stage's fb[0..3] and, after row i, fa[i].  So every fragment is read
+  // while the MFMAs of another one run, and the reads spread over the step.
   uint4 fa[WN], fb[WM];
 #pragma unroll
-  for (int j = 0; j < WM; ++j) fb[j] = frag_b(ring0, j);
+  for (int j = 0; j < WM / 2; ++j) fb[j] = frag_b(ring0, j);
 #pragma unroll
   for (int i = 0; i < WN; ++i) fa[i] = frag_a(ring0, i);
 
-  // Step U of a superfragment.  Row i of the 8 x 8 MFMA block also issues one
-  // fragment load of stage step+3 and reads the next step's fragments.  The flags
-  // drop the loads / reads of stages past the end in the peeled last
-  // superfragment (peeling keeps the loop body free of branches); VM is the
-  // number of vector-memory operations the step itself issues.  The scheduling
-  // barriers keep each row's memory operations between its MFMAs and stop the
-  // scheduler from interleaving rows, which would make the register allocator
-  // move accumulators around.
+  // Step U of a superfragment.  Row i also issues one fragment load of stage
+  // step+3.  The flags drop the loads / reads of stages past the end in the
+  // peeled last superfragment (peeling keeps the loop body free of branches);
+  // VM is the number of vector-memory operations the step itself issues.  The
+  // scheduling barriers keep each row's memory operations between its MFMAs
+  // and stop the scheduler from interleaving rows, which would make the
+  // register allocator move accumulators around.
 #define SVDQ_FP4_STEP(U, FETCH, READ, SCALES, VM)                                                     \
   {                                                                                                   \
     const int step = t0 + (U);                                                                        \
     uint4* const s3 = slot(((U) + 3) & 3);                                                            \
+    const uint4* const s0 = slot((U) & 3);                                                            \
     const uint4* const s1 = slot(((U) + 1) & 3);                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                \
     _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
       if (FETCH) fetch1(s3, step + 3, i);                                                             \
-      _Pragma("unroll") for (int j = 0; j < WM; ++j) {                                                \
+      _Pragma("unroll") for (int j = 0; j < WM / 2; ++j)                                              \
         acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
-        if ((READ) && i == WN - 1) fb[j] = frag_b(s1, j);                                             \
+      if (i % 2 == 1) fb[WM / 2 + i / 2] = frag_b(s0, WM / 2 + i / 2);                                \
+      __builtin_amdgcn_sched_barrier(0);                                                              \
+    }                                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
+      _Pragma("unroll") for (int j = WM / 2; j < WM; ++j)                                             \
+        acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
+      if (READ) {                                                                                     \
+        fa[i] = frag_a(s1, i);                                                                        \
+        if (i % 2 == 1) fb[i / 2] = frag_b(s1, i / 2);                                                \
       }                                                                                               \
-      if (READ) fa[i] = frag_a(s1, i);                                                                \
       __builtin_amdgcn_sched_barrier(0);                                                              \
     }                                                                                                 \
     if (SCALES) load_scales(san, sbn, sup + 1);                                                       \
