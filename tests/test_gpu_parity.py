@@ -133,6 +133,42 @@ def test_edge_values_bit_exact(torch_dev, fmt):
     assert np.all(np.isfinite(Y.cpu().numpy()))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+@pytest.mark.parametrize("lam_edge", ["inside", "outside"])
+def test_division_range_edges_bit_exact(torch_dev, fmt, lam_edge):
+    """Smoothing quotients at the edges of the range the activation kernel's
+    fast division accepts: |x| near 2^-40 and 2^60 with lambda at 2^-32 and
+    2^32 ("inside"), and a layer with some lambda outside [2^-32, 2^32], which
+    takes IEEE division everywhere ("outside").  Codes and scales must match the
+    oracle's IEEE fp32 quotients bit for bit."""
+    torch, dev = torch_dev
+    M, K, N, r = 48, 1024, 64, 16
+    spec, L = _medium_layer("qkv", fmt, M, K, N, r, 31)
+    rng = np.random.default_rng(77)
+    lam = L["lam"].copy()
+    if lam_edge == "inside":
+        lam[0], lam[1], lam[2], lam[3] = 2.0 ** -32, 2.0 ** 32, np.float32(2.0 ** -32 * 1.75), np.float32(2.0 ** 31 * 1.5)
+        lam[4:64] = np.exp2(rng.uniform(-32, 32, 60)).astype(np.float32)
+    else:
+        lam[5], lam[9] = 2.0 ** 40, 2.0 ** -40
+    L["lam"] = lam
+    X = L["X"].copy()
+    vals = np.array([2.0 ** -40, -(2.0 ** -40) * 1.5, 2.0 ** 60 * 0.99, -(2.0 ** 59) * 1.875, 2.0 ** -39,
+                     1.0, -3.0, 2.0 ** 59], np.float32)
+    X[0:8, 0:64] = synth.bf16_bits_from_f32(np.resize(vals, (8, 64)))
+    X[8:16] = synth.bf16_bits_from_f32(rng.standard_normal((8, K)).astype(np.float32)
+                                       * np.exp2(rng.integers(-38, 58, (8, K))).astype(np.float32))
+    L["X"] = X
+    layer = sq.Layer(fmt, K, N, r)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    ua = sq.unpack_act(layer, ws, M)
+    torch.cuda.synchronize()
+    cX, sX = Q.quantize(Ly.smooth(L["X"], L["lam"]), fmt)
+    assert_codes_equal(ua["codes"].cpu().numpy(), cX, f"activation codes ({lam_edge})")
+    assert_scales_equal(scales_np(ua["scales"], fmt), sX, f"activation scales ({lam_edge})")
+
+
 def test_epilogue_flags_separately(torch_dev):
     torch, dev = torch_dev
     spec, L = _medium_layer("qkv", "mxfp4", 96, 1024, 256, 32, 11)

@@ -37,18 +37,16 @@ __device__ __forceinline__ uint32_t cvt_bf2(float a, float b) {
 // makes the estimate faithful, the second gives the nearest-even quotient.  This
 // was checked against IEEE division for every bf16 dividend over 3000 divisors
 // and for 8e8 fp32 dividends over fp16-valued divisors, in the range
-// |a| >= 2^-80, 2^-100 <= |a / b| < 2^100.  Outside that range (zeros, tiny
-// values whose remainder would underflow, huge quotients) the caller falls back
-// to the IEEE division.
+// |a| >= 2^-80, 2^-100 <= |a / b| < 2^100 (it is Markstein's refinement
+// theorem: a faithful quotient refined once with the correctly rounded
+// reciprocal is the correctly rounded quotient, while nothing underflows).
+// Outside that range (zeros, tiny values whose remainder would underflow, huge
+// quotients) the caller uses the IEEE division.
 __device__ __forceinline__ float div_refined(float a, float b, float r) {
   float q = a * r;
   q = fmaf(fmaf(-q, b, a), r, q);
   q = fmaf(fmaf(-q, b, a), r, q);
   return q;
-}
-__device__ __forceinline__ bool div_refined_ok(float a, float q) {
-  const float aa = fabsf(a), aq = fabsf(q);
-  return aa >= 0x1p-80f && aq >= 0x1p-100f && aq < 0x1p100f;
 }
 
 // The E8M0 exponent byte of a group maximum: e = floor(log2 amax) - 2 clamped to
@@ -123,6 +121,14 @@ __device__ __forceinline__ float gelu_erf(float y) {
 // Hardware round-robins workgroups over the 8 XCDs (workgroup i runs on XCD i % 8).
 // Map the dispatch index to a logical tile index so that each XCD works on a
 // contiguous range of tiles (and so shares operands in its own L2).
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+// Buffer resource over [base, base + bytes): loads beyond the end return zero
+// and stores beyond it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int nx = 8;
   const int xcd = bid % nx, slot = bid / nx;

@@ -175,12 +175,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 
 constexpr int kStageFrags = 16;                 // fragments per operand per stage
 constexpr int kStageU4 = 2 * kStageFrags * 64;  // uint4 per stage (weights, then activations)
-constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
-
-// Buffer resource over [base, base + bytes): loads beyond the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
-}
 
 __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));

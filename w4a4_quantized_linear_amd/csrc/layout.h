@@ -31,24 +31,26 @@ constexpr int kKSuper = 512;       // K per scale superfragment; K must be a mul
 constexpr int kRankAlign = 32;     // rank padded to the bf16 MFMA K
 constexpr int kFmtMXFP4 = 1;
 constexpr int kFmtINT4 = 2;
+constexpr uint32_t kLamRangeBit = 1;   // weight flags: a lambda outside [2^-32, 2^32]
 
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 __host__ __device__ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
 
 struct WeightLayout {
   int64_t N_pad, r_pad;
-  size_t codes, scales, L1, L2, lam, rlam, bias, total;
+  size_t codes, scales, L1, L2, lam, rlam, bias, flags, total;
 };
 
 struct ActLayout {
   int64_t M_pad, r_pad;
-  int nw, splits;                  // activation kernel: waves per workgroup, K splits
+  int kr, splits;                  // activation kernel: K per workgroup, K splits (K / kr)
   size_t codes, scales, D, part, total;
 };
 
 // Codes: N_pad x K/2 bytes.  Scales: N_pad x K/32 bytes (E8M0 per 32, or fp16 per 64).
 // L1: K x r_pad bf16 (B fragments of the down projection).  L2: N_pad x r_pad bf16
 // (A fragments of the up projection).  lambda and 1/lambda: fp32[K].  bias: bf16[N_pad].
+// flags: uint32, bit 0 set when some lambda is outside [2^-32, 2^32] (see kLamRangeBit).
 __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   WeightLayout w;
   w.N_pad = round_up(N, kTileRows);
@@ -61,30 +63,33 @@ __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   w.lam = o;    o = align256(o + size_t(K) * 4);
   w.rlam = o;   o = align256(o + size_t(K) * 4);
   w.bias = o;   o = align256(o + size_t(w.N_pad) * 2);
+  w.flags = o;  o = align256(o + 4);
   w.total = o;
   return w;
 }
 
-constexpr int kActUnit = 256;      // K per wave work unit of the activation kernel
-constexpr int kActMaxWorkgroups = 4096;
+constexpr int kActRowTiles = 8;        // 16-row tiles (one per wave) per activation workgroup
+constexpr int kActLdsBytes = 65536;    // LDS for one workgroup's lambda, 1/lambda and L1 fragments
+constexpr int kActMinWorkgroups = 384; // fewer leave CUs idle
 
-// Work split of the activation kernel: each workgroup takes one 16-row tile and
-// one of `splits` equal K ranges, its `nw` waves striding over 256-K units of
-// that range.  Splits raise the workgroup count well past the CU count (so the
-// last wave of workgroups is small) at the cost of an fp32 partial of the down
-// projection per split, summed in fixed order by a second small kernel.
-__host__ __device__ inline void act_split(int K, int64_t M_pad, int* nw, int* splits) {
-  const int units = K / kActUnit;
-  int w = 1;
-  for (int c = 4; c >= 1; --c)
-    if (units % c == 0) { w = c; break; }
-  const int per = units / w;                     // units per wave with one split
-  const int64_t tiles = M_pad / 16;
-  int s = 1;
-  for (int d = per; d >= 1; --d)                 // most splits within the workgroup budget
-    if (per % d == 0 && tiles * d <= kActMaxWorkgroups) { s = d; break; }
-  *nw = w;
-  *splits = s;
+// Work split of the activation kernel: a workgroup takes kActRowTiles 16-row
+// tiles and one K range of kr (its lambda, 1/lambda and L1 fragments staged in
+// LDS, kr * (8 + 2 r_pad) bytes).  kr is the largest power of two dividing K
+// within the LDS budget, halved (down to 128) while the grid has fewer than
+// kActMinWorkgroups workgroups.  With more than one split, each workgroup
+// writes an fp32 partial of the down projection, summed in split order by a
+// second small kernel.
+__host__ __device__ inline void act_split(int K, int r_pad, int64_t M_pad, int* kr_out, int* splits) {
+  const int64_t groups = M_pad / (16 * kActRowTiles);
+  int kr = 64;
+  for (int c = 4096; c >= 64; c /= 2)
+    if (K % c == 0 && int64_t(c) * (8 + 2 * r_pad) <= kActLdsBytes) {
+      kr = c;
+      break;
+    }
+  while (kr > 128 && groups * (K / kr) < kActMinWorkgroups) kr /= 2;
+  *kr_out = kr;
+  *splits = K / kr;
 }
 
 // Codes: M_pad x K/2.  Scales: M_pad x K/32 bytes.  D: M_pad x r_pad x {hi, lo} bf16.
@@ -93,7 +98,7 @@ __host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
   ActLayout a;
   a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
   a.r_pad = round_up(rank, kRankAlign);
-  act_split(K, a.M_pad, &a.nw, &a.splits);
+  act_split(K, int(a.r_pad), a.M_pad, &a.kr, &a.splits);
   size_t o = 0;
   a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
   a.scales = o; o = align256(o + size_t(a.M_pad) * K / 32);

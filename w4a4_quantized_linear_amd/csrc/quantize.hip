@@ -106,14 +106,16 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
 
 // ---- launch 1 for activations ----
 //
-// Workgroup = one 16-row tile; its waves stride over 256-K units of K, and the
-// waves' partial down projections are summed in LDS at the end (fixed order).
-// Lane (row = lane % 16, c = lane / 16) holds 8 consecutive elements of each
+// Workgroup = kActRowTiles waves, one 16-row tile each, over one K range of kr
+// (a split of K).  The workgroup first stages lambda, 1/lambda and the L1
+// fragments of its K range in LDS; the only global loads in the main loop are
+// then the wave's own X, issued kActDepth steps ahead (loads complete in issue
+// order, so no other load ever waits behind the X prefetch).  Lane
+// (row = lane % 16, c = lane / 16) holds 8 consecutive elements of each
 // 32-element block: the A fragment of the bf16 16x16x32 MFMA, so the down
-// projection needs no data movement.  Within a unit the X loads run one 64-K step
-// ahead of the math; the smoothing divide is the refined reciprocal division
-// (same result as the IEEE division, far fewer operations); the group maximum
-// over the 4 lanes of a row uses the VALU lane swaps.
+// projection runs on the same registers.  The smoothing divide is the refined
+// reciprocal division (same result as IEEE division, far fewer operations); the
+// group maximum over the 4 lanes of a row uses the VALU lane swaps.
 
 __device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
   a[0] = bf_lo(r.x); a[1] = bf_hi(r.x); a[2] = bf_lo(r.y); a[3] = bf_hi(r.y);
@@ -130,214 +132,248 @@ __device__ __forceinline__ float rowgroup_max(float v) {
   return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// True when some of the 16 bf16 values has a biased exponent outside
+// [87, 187), i.e. |x| outside [2^-40, 2^60) (zeros and subnormals included):
+// per 16-bit half, ((bits & 0x7F80) - 0x2B80) mod 2^16 > 0x3180.
+__device__ __forceinline__ bool exp_out_of_range(const uint4& a, const uint4& b) {
+  const u16x2 lo = {0x2B80, 0x2B80};
+  auto f = [&](uint32_t v) { return __builtin_bit_cast(u16x2, v & 0x7F807F80u) - lo; };
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_elementwise_max(f(a.x), f(a.y)), __builtin_elementwise_max(f(a.z), f(a.w))),
+      __builtin_elementwise_max(__builtin_elementwise_max(f(b.x), f(b.y)), __builtin_elementwise_max(f(b.z), f(b.w))));
+  return (m.x > m.y ? m.x : m.y) > 0x3180;
+}
+
+constexpr int kActStep = 64;   // K per pipeline step: two 32-blocks (one INT4 group)
+constexpr int kActDepth = 3;   // steps of X in flight ahead of the one being computed
+
 // Register budget by down-projection width: waves per SIMD the compiler must
 // leave room for (the L1 fragments and accumulators grow with the rank).
 __host__ __device__ constexpr int act_min_waves(int r16) { return r16 <= 2 ? 4 : (r16 <= 8 ? 2 : 1); }
 
-// Grid: (16-row tiles, K splits); block: nw waves (nw <= 4).  With one split
-// the workgroup writes D; otherwise it writes its fp32 partial to `part` and
-// reduce_down_kernel sums the splits.
+// Grid: (row tiles / kActRowTiles, K splits); block: kActRowTiles waves;
+// dynamic LDS: kr * (8 + 2 r_pad) bytes.  With one split the waves write D;
+// otherwise their fp32 partials go to `part` and reduce_down_kernel sums them.
+// Loads and stores go through buffer resources with a per-wave base, so the
+// per-step addressing is a scalar offset (no 64-bit vector address math).
 template <int FMT, int R16>
-__global__ void __launch_bounds__(256, act_min_waves(R16)) quantize_act_kernel(
+__global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantize_act_kernel(
     const uint16_t* __restrict__ X, int64_t rows, int64_t ld, int K, const float* __restrict__ lam,
     const float* __restrict__ rlam, const uint4* __restrict__ L1f, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t rows_pad, uint16_t* __restrict__ Dout, float* __restrict__ part,
-    int r_pad) {
-  extern __shared__ float dred[];  // [NW][16][r_pad] partial down projections
+    int r_pad, int kr, const uint32_t* __restrict__ wflags) {
+  extern __shared__ uint4 smem[];  // lambda[kr], 1/lambda[kr] (fp32), then L1 fragments [kr/32][R16][64]
+  float* const slam = reinterpret_cast<float*>(smem);
+  float* const srlam = slam + kr;
+  uint4* const sl1 = smem + kr / 2;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, c = lane >> 4;
-  const int64_t rt = blockIdx.x;
+  const int64_t rt = int64_t(blockIdx.x) * kActRowTiles + w;
   const int split = blockIdx.y, nsplit = gridDim.y;
+  const int k_beg = split * kr;
   const int64_t m = rt * 16 + row;
-  const bool valid = m < rows;
-  const int nsuper = K / kKSuper;
-  const int per_split = (K / kActUnit) / nsplit;
-  const int u_beg = split * per_split, u_end = u_beg + per_split;
-  // Rows past the end read the last row (so no load is conditional, which
-  // keeps the compiler's wait counts exact) and use zeros instead.
-  const uint16_t* xr = X + (valid ? m : rows - 1) * ld + c * 8;
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  const int KS = K / kKStep, nsuper = K / kKSuper;
+  const int nsteps = kr / kActStep;
+
+  // Per-wave buffer views.  X: the tile's 16 rows from k_beg on; rows past the
+  // end read the last row (their codes are never read back: the GEMM drops
+  // those outputs and the unpacking stops at M).
+  const int64_t row0 = rt * 16 < rows ? rt * 16 : rows - 1;
+  const int64_t my_row = m < rows ? m : rows - 1;
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + row0 * ld + k_beg, uint32_t((16 * ld) * 2));
+  const uint32_t xoff = uint32_t((my_row - row0) * ld * 2 + c * 16);
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(codes + size_t(rt) * KS * 1024, uint32_t(KS) * 1024);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(scales + size_t(rt) * nsuper * 256, uint32_t(nsuper) * 256);
+  auto load_x = [&](int p, uint4& lo, uint4& hi) {
+    const int q = p < nsteps ? p : nsteps - 1;   // past the end: an in-bounds load that is never used
+    lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff, uint32_t(q) * 128, 0));
+    hi = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff, uint32_t(q) * 128 + 64, 0));
+  };
+
+  // X of the first kActDepth steps, then the LDS staging of this K range.
+  uint4 xs[kActDepth + 1][2];
+#pragma unroll
+  for (int j = 0; j < kActDepth; ++j) load_x(j, xs[j][0], xs[j][1]);
+  for (int i = threadIdx.x; i < kr / 4; i += blockDim.x) {
+    reinterpret_cast<float4*>(slam)[i] = reinterpret_cast<const float4*>(lam + k_beg)[i];
+    reinterpret_cast<float4*>(srlam)[i] = reinterpret_cast<const float4*>(rlam + k_beg)[i];
+  }
+  if (R16 > 0) {
+    const uint4* src = L1f + size_t(k_beg / 32) * R16 * 64;
+    for (int i = threadIdx.x; i < (kr / 32) * R16 * 64; i += blockDim.x) sl1[i] = src[i];
+  }
+  __syncthreads();
 
   v4f dacc[R16 > 0 ? R16 : 1];
 #pragma unroll
   for (int i = 0; i < (R16 > 0 ? R16 : 1); ++i) dacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 cur0 = *reinterpret_cast<const uint4*>(xr + (u_beg + w) * kActUnit);
-  uint4 cur1 = *reinterpret_cast<const uint4*>(xr + (u_beg + w) * kActUnit + 32);
-  for (int u = u_beg + w; u < u_end; u += nw) {
-    const int k0 = u * kActUnit;
-    // First K of the wave's next unit (the last unit again when there is none:
-    // an in-bounds load whose value is never used).
-    const int kn = (u + nw < u_end ? u + nw : u_end - 1) * kActUnit;
-    if (!valid) cur0 = cur1 = zero4;
-    uint32_t sw = 0;  // MXFP4: this lane's two scale bytes of the unit
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {  // 64-element steps of the unit
-      // This step's lambda, 1/lambda and L1 fragments first, then the next
-      // step's X: loads complete in issue order, so waiting for the small
-      // cached loads never waits for the X prefetch behind them.
-      float4 lq[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = k0 + (2 * p + h) * 32 + c * 8;
-        lq[h][0] = *reinterpret_cast<const float4*>(lam + k);
-        lq[h][1] = *reinterpret_cast<const float4*>(lam + k + 4);
-        lq[h][2] = *reinterpret_cast<const float4*>(rlam + k);
-        lq[h][3] = *reinterpret_cast<const float4*>(rlam + k + 4);
-      }
-      uint4 l1b[2][R16 > 0 ? R16 : 1];
-      if (R16 > 0) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4* bf = L1f + (size_t(u * 8 + 2 * p + h) * R16) * 64 + lane;
-#pragma unroll
-          for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) l1b[h][ib] = bf[ib * 64];
-        }
-      }
-      uint4 nxt0 = make_uint4(0u, 0u, 0u, 0u), nxt1 = nxt0;
-      float x[16];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float lv[8] = {lq[h][0].x, lq[h][0].y, lq[h][0].z, lq[h][0].w,
-                             lq[h][1].x, lq[h][1].y, lq[h][1].z, lq[h][1].w};
-        const float rv[8] = {lq[h][2].x, lq[h][2].y, lq[h][2].z, lq[h][2].w,
-                             lq[h][3].x, lq[h][3].y, lq[h][3].z, lq[h][3].w};
-        float a[8];
-        unpack_bf8(h == 0 ? cur0 : cur1, a);
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[8 * h + e] = div_refined(a[e], lv[e], rv[e]);
-          ok = ok && div_refined_ok(a[e], x[8 * h + e]);
-        }
-        if (!ok) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[8 * h + e] = a[e] / lv[e];
-        }
-        if (h == 0) {
-          // The next step's X goes out once the first half no longer needs
-          // its registers.
-          __builtin_amdgcn_sched_barrier(0);
-          const int kx = p < 3 ? k0 + (2 * p + 2) * 32 : kn;
-          nxt0 = *reinterpret_cast<const uint4*>(xr + kx);
-          nxt1 = *reinterpret_cast<const uint4*>(xr + kx + 32);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+  // Division path of the layer: the refined division when every lambda is in
+  // [2^-32, 2^32], else IEEE division everywhere (uniform for the launch).
+  const bool ieee_only = (__builtin_amdgcn_readfirstlane(*wflags) & kLamRangeBit) != 0;
 
-      if (FMT == kFmtMXFP4) {
+  // One 64-K step on the X held in (xa, xb).
+  auto step = [&](int p, const uint4& xa, const uint4& xb) {
+    const int kl = p * kActStep;                  // K offset inside the range
+    // The refined division (and, for INT4, the second one by the group scale)
+    // equals the IEEE quotient when |x| is in [2^-40, 2^60) and lambda in
+    // [2^-32, 2^32]: every quotient and remainder then stays far inside the
+    // normal range.  Checked on the bf16 exponent fields, two per dword: the
+    // biased exponent must lie in [87, 187), i.e. (bits & 0x7F80) - 0x2B80,
+    // taken modulo 2^16, is at most 0x3180.  Zeros and subnormals fail too.
+    const bool fast = !ieee_only && !__any(exp_out_of_range(xa, xb));
+    float x[16];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int jb = 2 * p + h;                 // block within the unit
-          float amax = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const float4* lq = reinterpret_cast<const float4*>(slam + kl + h * 32 + c * 8);
+      const float4* rq = reinterpret_cast<const float4*>(srlam + kl + h * 32 + c * 8);
+      const float4 l0 = lq[0], l1 = lq[1], q0 = rq[0], q1 = rq[1];
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float rv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      float a[8];
+      unpack_bf8(h == 0 ? xa : xb, a);
+      if (__builtin_expect(fast, 1)) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
-          amax = rowgroup_max(amax);
-          const uint32_t sb = e8m0_of_amax(amax);
-          const float inv = inv_scale_of_e8m0(sb);
-          uint32_t cw = 0;
-          cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
-          cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
-          cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
-          cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
-          const int ks = u * 2 + jb / 4;            // 128-K step
-          *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (jb & 3) * 16 + row) + c * 4) = cw;
-          if ((jb & 3) == c) sw |= sb << (8 * (jb >> 2));
-        }
+        for (int e = 0; e < 8; ++e) x[8 * h + e] = div_refined(a[e], lv[e], rv[e]);
       } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * h + e] = a[e] / lv[e];
+      }
+    }
+
+    const int kb0 = (k_beg + kl) / 32;            // global 32-block index of the step's first block
+    const int ks = kb0 / 4;                       // 128-K step
+    if (FMT == kFmtMXFP4) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = kb0 + h;
         float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
         amax = rowgroup_max(amax);
-        const float s32 = amax / 7.0f;
-        const _Float16 h16 = (_Float16)fminf(s32, 65504.0f);
-        const float sc = (float)h16;
-        const float rs = 1.0f / sc;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float t[8];
-          bool ok = true;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            t[e] = div_refined(x[8 * h + e], sc, rs);
-            ok = ok && div_refined_ok(x[8 * h + e], t[e]);
-          }
-          if (!ok) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = x[8 * h + e] / sc;
-          }
-          uint32_t cw = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float tq = __builtin_rintf(fminf(fmaxf(t[e], -8.0f), 7.0f));
-            const int q = (sc == 0.0f) ? 0 : int(tq);
-            cw |= (uint32_t(q) & 0xFu) << (4 * e);
-          }
-          const int jb = 2 * p + h;
-          const int kk = (jb & 3) * 32 + c * 8;    // offset inside the 128-K step
-          const int gi = kk / 64, o = kk % 64;
-          const int ks = u * 2 + jb / 4;
-          *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (o / 16) * 16 + row) + gi * 8 + (o % 16) / 2) = cw;
-        }
-        if (c == 0) {
-          const int g = u * 4 + p;
-          *reinterpret_cast<_Float16*>(scales + i4_scale_byte(m, g, rows_pad)) = h16;
-        }
+        const uint32_t sb = e8m0_of_amax(amax);
+        const float inv = inv_scale_of_e8m0(sb);
+        uint32_t cw = 0;
+        cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
+        cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
+        cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
+        cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+        // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
+        __builtin_amdgcn_raw_buffer_store_b32(cw, rC, uint32_t(row * 16 + c * 4),
+                                              uint32_t(ks * 1024 + (kb & 3) * 256), 0);
+        // the scale of (row, block kb & 3 of its 128-K step) is byte ks % 4 of
+        // that lane's superfragment dword: this lane when c == kb & 3
+        if (c == (kb & 3))
+          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sb), rS, uint32_t(lane * 4), uint32_t((kb / 16) * 256 + ks % 4),
+                                               0);
       }
-
-      if (R16 > 0) {
-        // Down projection: x_hat as a bf16 hi + lo pair (about 16 significant
-        // bits) against the bf16 L1, accumulated in fp32.
+    } else {
+      float amax = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint4 hi, lo;
-          hi.x = cvt_bf2(x[8 * h + 0], x[8 * h + 1]);
-          hi.y = cvt_bf2(x[8 * h + 2], x[8 * h + 3]);
-          hi.z = cvt_bf2(x[8 * h + 4], x[8 * h + 5]);
-          hi.w = cvt_bf2(x[8 * h + 6], x[8 * h + 7]);
-          lo.x = cvt_bf2(x[8 * h + 0] - bf_lo(hi.x), x[8 * h + 1] - bf_hi(hi.x));
-          lo.y = cvt_bf2(x[8 * h + 2] - bf_lo(hi.y), x[8 * h + 3] - bf_hi(hi.y));
-          lo.z = cvt_bf2(x[8 * h + 4] - bf_lo(hi.z), x[8 * h + 5] - bf_hi(hi.z));
-          lo.w = cvt_bf2(x[8 * h + 6] - bf_lo(hi.w), x[8 * h + 7] - bf_hi(hi.w));
+      for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      amax = rowgroup_max(amax);
+      const float s32 = amax / 7.0f;
+      const _Float16 h16 = (_Float16)fminf(s32, 65504.0f);
+      const float sc = (float)h16;
+      const float rs = 1.0f / sc;
+      const int g = kb0 / 2, gi = g & 1;          // 64-group and its index in the 128-K step
 #pragma unroll
-          for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) {
-            dacc[ib] = mfma_bf16(hi, l1b[h][ib], dacc[ib]);
-            dacc[ib] = mfma_bf16(lo, l1b[h][ib], dacc[ib]);
-          }
+      for (int h = 0; h < 2; ++h) {
+        // a zero scale (every x of the group rounds it to 0) gives codes 0
+        // whatever t is, so the quotient only matters for a positive scale
+        float t[8];
+        if (__builtin_expect(fast, 1)) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = div_refined(x[8 * h + e], sc, rs);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = x[8 * h + e] / sc;
         }
+        uint32_t cw = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float tq = __builtin_rintf(fminf(fmaxf(t[e], -8.0f), 7.0f));
+          const int q = (sc == 0.0f) ? 0 : int(tq);
+          cw |= (uint32_t(q) & 0xFu) << (4 * e);
+        }
+        // group offset o = 32h + 8c: lane chunk (o / 16) * 16 + row, bytes 8 gi + (o % 16) / 2
+        __builtin_amdgcn_raw_buffer_store_b32(cw, rC, uint32_t((c / 2) * 256 + row * 16 + (c % 2) * 4),
+                                              uint32_t(ks * 1024 + h * 512 + gi * 8), 0);
       }
-      cur0 = valid ? nxt0 : zero4;
-      cur1 = valid ? nxt1 : zero4;
+      if (c == 0) *reinterpret_cast<_Float16*>(scales + i4_scale_byte(m, g, rows_pad)) = h16;
     }
-    if (FMT == kFmtMXFP4)
-      *reinterpret_cast<uint16_t*>(scales + (size_t(rt) * nsuper + u / 2) * 256 + lane * 4 + (u & 1) * 2) =
-          uint16_t(sw);
+
+    if (R16 > 0) {
+      // Down projection: x_hat as a bf16 hi + lo pair (about 16 significant
+      // bits) against the bf16 L1, accumulated in fp32.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 hi, lo;
+        hi.x = cvt_bf2(x[8 * h + 0], x[8 * h + 1]);
+        hi.y = cvt_bf2(x[8 * h + 2], x[8 * h + 3]);
+        hi.z = cvt_bf2(x[8 * h + 4], x[8 * h + 5]);
+        hi.w = cvt_bf2(x[8 * h + 6], x[8 * h + 7]);
+        lo.x = cvt_bf2(x[8 * h + 0] - bf_lo(hi.x), x[8 * h + 1] - bf_hi(hi.x));
+        lo.y = cvt_bf2(x[8 * h + 2] - bf_lo(hi.y), x[8 * h + 3] - bf_hi(hi.y));
+        lo.z = cvt_bf2(x[8 * h + 4] - bf_lo(hi.z), x[8 * h + 5] - bf_hi(hi.z));
+        lo.w = cvt_bf2(x[8 * h + 6] - bf_lo(hi.w), x[8 * h + 7] - bf_hi(hi.w));
+        const uint4* bf = sl1 + size_t((2 * p + h) * R16) * 64 + lane;
+#pragma unroll
+        for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib) {
+          const uint4 b = bf[ib * 64];
+          dacc[ib] = mfma_bf16(hi, b, dacc[ib]);
+          dacc[ib] = mfma_bf16(lo, b, dacc[ib]);
+        }
+      }
+    }
+  };
+
+  // X stages form a ring of kActDepth + 1 register sets: step p uses set p % 4
+  // and refills the set of step p - 1 with step p + 3.  Four steps per
+  // iteration keep the set indices compile-time; a range of 1 or 2 steps
+  // (large ranks) takes the short loop that rotates the sets instead.
+  static_assert(kActDepth == 3, "ring of four register sets");
+  if (nsteps % 4 == 0) {
+    for (int p = 0; p < nsteps; p += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        load_x(p + j + 3, xs[(j + 3) & 3][0], xs[(j + 3) & 3][1]);
+        step(p + j, xs[j][0], xs[j][1]);
+      }
+    }
+  } else {
+    for (int p = 0; p < nsteps; ++p) {
+      load_x(p + 3, xs[3][0], xs[3][1]);
+      step(p, xs[0][0], xs[0][1]);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        xs[j][0] = xs[j + 1][0];
+        xs[j][1] = xs[j + 1][1];
+      }
+    }
   }
 
   if (R16 > 0) {
-    // Reduce the waves' partial sums in a fixed order (deterministic), then store
-    // D as bf16 hi + lo in the up projection's B-fragment layout.
+    // Lane holds rows (lane / 16) * 4 + e, column ib * 16 + lane % 16 of its tile.
 #pragma unroll
     for (int ib = 0; ib < (R16 > 0 ? R16 : 1); ++ib)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dred[(w * 16 + (lane >> 4) * 4 + e) * r_pad + ib * 16 + (lane & 15)] = dacc[ib][e];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * r_pad; idx += blockDim.x) {
-      const int rr = idx / r_pad, col = idx % r_pad;
-      float s = 0.f;
-      for (int ww = 0; ww < nw; ++ww) s += dred[(ww * 16 + rr) * r_pad + col];
-      if (nsplit > 1) {
-        part[((size_t(split) * rows_pad) + rt * 16) * r_pad + idx] = s;
-      } else {
-        const uint32_t hb = f2bf(s);
-        const uint32_t lb = f2bf(s - bf_lo(hb));
-        const int64_t mm = rt * 16 + rr;
-        Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
-        Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+      for (int e = 0; e < 4; ++e) {
+        const int64_t mm = rt * 16 + (lane >> 4) * 4 + e;
+        const int col = ib * 16 + (lane & 15);
+        const float v = dacc[ib][e];
+        if (nsplit > 1) {
+          part[(size_t(split) * rows_pad + mm) * r_pad + col] = v;
+        } else {
+          const uint32_t hb = f2bf(v);
+          const uint32_t lb = f2bf(v - bf_lo(hb));
+          Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
+          Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+        }
       }
-    }
   }
 }
 
@@ -398,6 +434,27 @@ __global__ void pack_vec_kernel(const float* __restrict__ lam, int K, const uint
     rlam_out[i] = 1.0f / lam[i];
   }
   if (i < N_pad) bias_out[i] = (bias != nullptr && i < N) ? bias[i] : uint16_t(0);
+}
+
+// Flags word of the packed weights: kLamRangeBit when some lambda is outside
+// [2^-32, 2^32] (or not finite).  Inside that range the activation kernel's
+// refined division is exact for every input it lets through (see its range
+// check); otherwise the layer takes the IEEE division throughout.  One
+// workgroup; a fixed-order reduction, so no prior zeroing is needed.
+__global__ void check_lambda_kernel(const float* __restrict__ lam, int K, uint32_t* __restrict__ flags) {
+  __shared__ uint32_t red[256];
+  uint32_t bad = 0;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const float v = lam[i];
+    bad |= (v >= 0x1p-32f && v <= 0x1p32f) ? 0u : kLamRangeBit;   // false for NaN too
+  }
+  red[threadIdx.x] = bad;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w /= 2) {
+    if (int(threadIdx.x) < w) red[threadIdx.x] |= red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *flags = red[0];
 }
 
 // ---- test-only unpackers to the canonical layout ----
@@ -463,14 +520,14 @@ static int pick_waves(int K) {
 template <int FMT>
 static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
                                           const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales,
-                                          int64_t rows_pad, uint16_t* Dout, float* part, int r_pad, int nw,
-                                          int splits, hipStream_t s) {
-  const dim3 grid(unsigned(rows_pad / 16), unsigned(splits)), block(unsigned(64 * nw));
-  const size_t shm = size_t(nw) * 16 * r_pad * 4;
+                                          int64_t rows_pad, uint16_t* Dout, float* part, int r_pad, int kr,
+                                          int splits, const uint32_t* wflags, hipStream_t s) {
+  const dim3 grid(unsigned(rows_pad / (16 * kActRowTiles)), unsigned(splits)), block(64 * kActRowTiles);
+  const size_t shm = size_t(kr) * (8 + 2 * r_pad);
   const uint4* l1 = reinterpret_cast<const uint4*>(L1f);
 #define SVDQ_QA(R16)                                                                                      \
   hipLaunchKernelGGL((quantize_act_kernel<FMT, R16>), grid, block, shm, s, X, rows, ld, K, lam, rlam, l1, \
-                     codes, scales, rows_pad, Dout, part, r_pad)
+                     codes, scales, rows_pad, Dout, part, r_pad, kr, wflags)
   switch (r_pad / 16) {
     case 0: SVDQ_QA(0); break;
     case 2: SVDQ_QA(2); break;
@@ -494,12 +551,13 @@ static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
                                const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
-                               uint16_t* Dout, float* part, int r_pad, int nw, int splits, hipStream_t s) {
+                               uint16_t* Dout, float* part, int r_pad, int kr, int splits, const uint32_t* wflags,
+                               hipStream_t s) {
   if (fmt == kFmtMXFP4)
     return launch_quantize_act_fmt<kFmtMXFP4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
-                                              r_pad, nw, splits, s);
+                                              r_pad, kr, splits, wflags, s);
   return launch_quantize_act_fmt<kFmtINT4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
-                                           r_pad, nw, splits, s);
+                                           r_pad, kr, splits, wflags, s);
 }
 
 hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
@@ -532,6 +590,8 @@ hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* 
   hipLaunchKernelGGL(pack_vec_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, lam, K, bias, N, wl.N_pad,
                      reinterpret_cast<float*>(blob + wl.lam), reinterpret_cast<float*>(blob + wl.rlam),
                      reinterpret_cast<uint16_t*>(blob + wl.bias));
+  hipLaunchKernelGGL(check_lambda_kernel, dim3(1), dim3(256), 0, s, lam, K,
+                     reinterpret_cast<uint32_t*>(blob + wl.flags));
   return hipGetLastError();
 }
 
