@@ -12,7 +12,8 @@ namespace svdq {
 hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
                                   uint8_t* scales, int64_t rows_pad, hipStream_t s);
 hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
-                               const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
+                               const float* rlam, const float* rlo, const void* L1f, uint8_t* codes, uint8_t* scales,
+                               int64_t rows_pad,
                                uint16_t* Dout, float* part, int r_pad, int kr, int splits, const uint32_t* wflags,
                                hipStream_t s);
 hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* lam, const uint16_t* bias, int K,
@@ -159,7 +160,8 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* d, const void* w_packed, co
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
   uint8_t* ws = static_cast<uint8_t*>(a_packed);
   return launched(launch_quantize_act(d->fmt, X, M, ldx, d->K, reinterpret_cast<const float*>(blob + wl.lam),
-                                      reinterpret_cast<const float*>(blob + wl.rlam), blob + wl.L1, ws + al.codes,
+                                      reinterpret_cast<const float*>(blob + wl.rlam),
+                                      reinterpret_cast<const float*>(blob + wl.rlo), blob + wl.L1, ws + al.codes,
                                       ws + al.scales, al.M_pad, reinterpret_cast<uint16_t*>(ws + al.D),
                                       reinterpret_cast<float*>(ws + al.part), int(al.r_pad), al.kr, al.splits,
                                       reinterpret_cast<const uint32_t*>(blob + wl.flags),

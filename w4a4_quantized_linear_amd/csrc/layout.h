@@ -32,13 +32,14 @@ constexpr int kRankAlign = 32;     // rank padded to the bf16 MFMA K
 constexpr int kFmtMXFP4 = 1;
 constexpr int kFmtINT4 = 2;
 constexpr uint32_t kLamRangeBit = 1;   // weight flags: a lambda outside [2^-32, 2^32]
+constexpr uint32_t kDivSlowBit = 2;    // weight flags: the two-operation division is not exact for some lambda
 
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 __host__ __device__ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
 
 struct WeightLayout {
   int64_t N_pad, r_pad;
-  size_t codes, scales, L1, L2, lam, rlam, bias, flags, total;
+  size_t codes, scales, L1, L2, lam, rlam, rlo, bias, flags, total;
 };
 
 struct ActLayout {
@@ -49,8 +50,9 @@ struct ActLayout {
 
 // Codes: N_pad x K/2 bytes.  Scales: N_pad x K/32 bytes (E8M0 per 32, or fp16 per 64).
 // L1: K x r_pad bf16 (B fragments of the down projection).  L2: N_pad x r_pad bf16
-// (A fragments of the up projection).  lambda and 1/lambda: fp32[K].  bias: bf16[N_pad].
-// flags: uint32, bit 0 set when some lambda is outside [2^-32, 2^32] (see kLamRangeBit).
+// (A fragments of the up projection).  lambda, r = RN(1/lambda) and the correction
+// rl = RN((1 - r lambda) r): fp32[K] each.  bias: bf16[N_pad].  flags: uint32
+// (kLamRangeBit, kDivSlowBit).
 __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   WeightLayout w;
   w.N_pad = round_up(N, kTileRows);
@@ -62,6 +64,7 @@ __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   w.L2 = o;     o = align256(o + size_t(w.N_pad) * w.r_pad * 2);
   w.lam = o;    o = align256(o + size_t(K) * 4);
   w.rlam = o;   o = align256(o + size_t(K) * 4);
+  w.rlo = o;    o = align256(o + size_t(K) * 4);
   w.bias = o;   o = align256(o + size_t(w.N_pad) * 2);
   w.flags = o;  o = align256(o + 4);
   w.total = o;
@@ -69,12 +72,12 @@ __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
 }
 
 constexpr int kActRowTiles = 8;        // 16-row tiles (one per wave) per activation workgroup
-constexpr int kActLdsBytes = 65536;    // LDS for one workgroup's lambda, 1/lambda and L1 fragments
+constexpr int kActLdsBytes = 65536;    // LDS for one workgroup's lambda, r, rl and L1 fragments
 constexpr int kActMinWorkgroups = 384; // fewer leave CUs idle
 
 // Work split of the activation kernel: a workgroup takes kActRowTiles 16-row
-// tiles and one K range of kr (its lambda, 1/lambda and L1 fragments staged in
-// LDS, kr * (8 + 2 r_pad) bytes).  kr is the largest power of two dividing K
+// tiles and one K range of kr (its lambda, r, rl and L1 fragments staged in
+// LDS, kr * (12 + 2 r_pad) bytes).  kr is the largest power of two dividing K
 // within the LDS budget, halved (down to 128) while the grid has fewer than
 // kActMinWorkgroups workgroups.  With more than one split, each workgroup
 // writes an fp32 partial of the down projection, summed in split order by a
@@ -83,7 +86,7 @@ __host__ __device__ inline void act_split(int K, int r_pad, int64_t M_pad, int* 
   const int64_t groups = M_pad / (16 * kActRowTiles);
   int kr = 64;
   for (int c = 4096; c >= 64; c /= 2)
-    if (K % c == 0 && int64_t(c) * (8 + 2 * r_pad) <= kActLdsBytes) {
+    if (K % c == 0 && int64_t(c) * (12 + 2 * r_pad) <= kActLdsBytes) {
       kr = c;
       break;
     }

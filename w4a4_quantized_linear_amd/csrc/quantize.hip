@@ -161,13 +161,14 @@ __host__ __device__ constexpr int act_min_waves(int r16) { return r16 <= 2 ? 4 :
 template <int FMT, int R16>
 __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantize_act_kernel(
     const uint16_t* __restrict__ X, int64_t rows, int64_t ld, int K, const float* __restrict__ lam,
-    const float* __restrict__ rlam, const uint4* __restrict__ L1f, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t rows_pad, uint16_t* __restrict__ Dout, float* __restrict__ part,
-    int r_pad, int kr, const uint32_t* __restrict__ wflags) {
-  extern __shared__ uint4 smem[];  // lambda[kr], 1/lambda[kr] (fp32), then L1 fragments [kr/32][R16][64]
+    const float* __restrict__ rlam, const float* __restrict__ rlo, const uint4* __restrict__ L1f,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t rows_pad, uint16_t* __restrict__ Dout,
+    float* __restrict__ part, int r_pad, int kr, const uint32_t* __restrict__ wflags) {
+  extern __shared__ uint4 smem[];  // lambda[kr], r[kr], rl[kr] (fp32), then L1 fragments [kr/32][R16][64]
   float* const slam = reinterpret_cast<float*>(smem);
   float* const srlam = slam + kr;
-  uint4* const sl1 = smem + kr / 2;
+  float* const srlo = srlam + kr;
+  uint4* const sl1 = smem + 3 * kr / 4;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane & 15, c = lane >> 4;
@@ -200,6 +201,7 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
   for (int i = threadIdx.x; i < kr / 4; i += blockDim.x) {
     reinterpret_cast<float4*>(slam)[i] = reinterpret_cast<const float4*>(lam + k_beg)[i];
     reinterpret_cast<float4*>(srlam)[i] = reinterpret_cast<const float4*>(rlam + k_beg)[i];
+    reinterpret_cast<float4*>(srlo)[i] = reinterpret_cast<const float4*>(rlo + k_beg)[i];
   }
   if (R16 > 0) {
     const uint4* src = L1f + size_t(k_beg / 32) * R16 * 64;
@@ -211,34 +213,47 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
 #pragma unroll
   for (int i = 0; i < (R16 > 0 ? R16 : 1); ++i) dacc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Division path of the layer: the refined division when every lambda is in
-  // [2^-32, 2^32], else IEEE division everywhere (uniform for the launch).
-  const bool ieee_only = (__builtin_amdgcn_readfirstlane(*wflags) & kLamRangeBit) != 0;
+  // Division path of the layer (uniform for the launch): with every lambda in
+  // [2^-32, 2^32], the two-operation quotient fma(x, r, x rl) when the weight
+  // packing verified it exact for every lambda, else the refined division;
+  // with some lambda outside that range, IEEE division everywhere.
+  const uint32_t wf = __builtin_amdgcn_readfirstlane(*wflags);
+  const bool ieee_only = (wf & kLamRangeBit) != 0;
+  const bool div2 = (wf & kDivSlowBit) == 0;
 
   // One 64-K step on the X held in (xa, xb).
   auto step = [&](int p, const uint4& xa, const uint4& xb) {
     const int kl = p * kActStep;                  // K offset inside the range
-    // The refined division (and, for INT4, the second one by the group scale)
-    // equals the IEEE quotient when |x| is in [2^-40, 2^60) and lambda in
-    // [2^-32, 2^32]: every quotient and remainder then stays far inside the
-    // normal range.  Checked on the bf16 exponent fields, two per dword: the
-    // biased exponent must lie in [87, 187), i.e. (bits & 0x7F80) - 0x2B80,
-    // taken modulo 2^16, is at most 0x3180.  Zeros and subnormals fail too.
+    // The fast divisions (and, for INT4, the refined division by the group
+    // scale) equal the IEEE quotient when |x| is in [2^-40, 2^60) and lambda in
+    // [2^-32, 2^32]: every product, quotient and remainder then stays far inside
+    // the normal range.  Checked on the bf16 exponent fields, two per dword: the
+    // biased exponent must lie in [87, 187).  Zeros and subnormals fail too.
     const bool fast = !ieee_only && !__any(exp_out_of_range(xa, xb));
     float x[16];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float4* lq = reinterpret_cast<const float4*>(slam + kl + h * 32 + c * 8);
-      const float4* rq = reinterpret_cast<const float4*>(srlam + kl + h * 32 + c * 8);
-      const float4 l0 = lq[0], l1 = lq[1], q0 = rq[0], q1 = rq[1];
-      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-      const float rv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      float a[8];
+      const int ko = kl + h * 32 + c * 8;
+      auto ld8 = [&](const float* v, float (&o)[8]) {
+        const float4 u0 = *reinterpret_cast<const float4*>(v + ko), u1 = *reinterpret_cast<const float4*>(v + ko + 4);
+        o[0] = u0.x; o[1] = u0.y; o[2] = u0.z; o[3] = u0.w; o[4] = u1.x; o[5] = u1.y; o[6] = u1.z; o[7] = u1.w;
+      };
+      float a[8], r[8];
       unpack_bf8(h == 0 ? xa : xb, a);
-      if (__builtin_expect(fast, 1)) {
+      ld8(srlam, r);
+      if (__builtin_expect(fast && div2, 1)) {
+        float rl[8];
+        ld8(srlo, rl);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * h + e] = div_refined(a[e], lv[e], rv[e]);
+        for (int e = 0; e < 8; ++e) x[8 * h + e] = fmaf(a[e], r[e], a[e] * rl[e]);
+      } else if (fast) {
+        float lv[8];
+        ld8(slam, lv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * h + e] = div_refined(a[e], lv[e], r[e]);
       } else {
+        float lv[8];
+        ld8(slam, lv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[8 * h + e] = a[e] / lv[e];
       }
@@ -378,20 +393,40 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
 }
 
 // Sum of the K splits' partial down projections, in split order, stored as
-// the bf16 hi + lo pair the GEMM epilogue reads.
+// the bf16 hi + lo pair the GEMM epilogue reads.  Each thread takes 4
+// consecutive columns; the loads of 4 splits go out before their sums.
 __global__ void reduce_down_kernel(const float* __restrict__ part, int splits, int64_t rows_pad, int r_pad,
                                    uint16_t* __restrict__ Dout) {
   const int64_t total = rows_pad * r_pad;
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  float s = 0.f;
-  for (int sp = 0; sp < splits; ++sp) s += part[size_t(sp) * total + i];
-  const uint32_t hb = f2bf(s);
-  const uint32_t lb = f2bf(s - bf_lo(hb));
-  const int64_t mm = i / r_pad;
-  const int col = int(i % r_pad);
-  Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
-  Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+  const int64_t i4 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= total) return;
+  const float4* src = reinterpret_cast<const float4*>(part + i4);
+  const int64_t stride = total / 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sp = 0;
+  for (; sp + 4 <= splits; sp += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[(sp + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+    }
+  }
+  for (; sp < splits; ++sp) {
+    const float4 v = src[sp * stride];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const float vals[4] = {s.x, s.y, s.z, s.w};
+  const int64_t mm = i4 / r_pad;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int col = int(i4 % r_pad) + e;
+    const uint32_t hb = f2bf(vals[e]);
+    const uint32_t lb = f2bf(vals[e] - bf_lo(hb));
+    Dout[d_elem(mm, col, 0, r_pad)] = uint16_t(hb);
+    Dout[d_elem(mm, col, 1, r_pad)] = uint16_t(lb);
+  }
 }
 
 // ---- packing of the small operands (load time) ----
@@ -427,26 +462,46 @@ __global__ void pack_l2_kernel(const uint16_t* __restrict__ L2, int N, int64_t N
 
 __global__ void pack_vec_kernel(const float* __restrict__ lam, int K, const uint16_t* __restrict__ bias, int N,
                                 int64_t N_pad, float* __restrict__ lam_out, float* __restrict__ rlam_out,
-                                uint16_t* __restrict__ bias_out) {
+                                float* __restrict__ rlo_out, uint16_t* __restrict__ bias_out) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < K) {
-    lam_out[i] = lam[i];
-    rlam_out[i] = 1.0f / lam[i];
+    const float v = lam[i];
+    const float r = 1.0f / v;                    // RN(1/lambda)
+    lam_out[i] = v;
+    rlam_out[i] = r;
+    rlo_out[i] = fmaf(-r, v, 1.0f) * r;          // (1 - r lambda) is exact; rl ~ 1/lambda - r
   }
   if (i < N_pad) bias_out[i] = (bias != nullptr && i < N) ? bias[i] : uint16_t(0);
 }
 
-// Flags word of the packed weights: kLamRangeBit when some lambda is outside
-// [2^-32, 2^32] (or not finite).  Inside that range the activation kernel's
-// refined division is exact for every input it lets through (see its range
-// check); otherwise the layer takes the IEEE division throughout.  One
-// workgroup; a fixed-order reduction, so no prior zeroing is needed.
-__global__ void check_lambda_kernel(const float* __restrict__ lam, int K, uint32_t* __restrict__ flags) {
-  __shared__ uint32_t red[256];
+// Flags word of the packed weights, for the activation kernel's smoothing divide
+// x / lambda of bf16 x:
+//   kLamRangeBit: some lambda outside [2^-32, 2^32] (or not finite); the layer
+//     then takes the IEEE division throughout.
+//   kDivSlowBit: for some lambda the two-operation quotient fma(x, r, x rl)
+//     differs from the IEEE quotient for some bf16 x; the layer then takes the
+//     refined division (five operations) instead.  The check covers every bf16
+//     mantissa (x = m / 128, m in [128, 256)); scaling x by a power of two
+//     scales every step exactly while nothing under- or overflows, which the
+//     kernel's exponent range check ensures, and the sign is symmetric.
+// One workgroup; a fixed-order reduction, so no prior zeroing is needed.
+__global__ void __launch_bounds__(1024) check_lambda_kernel(const float* __restrict__ lam,
+                                                            const float* __restrict__ rlam,
+                                                            const float* __restrict__ rlo, int K,
+                                                            uint32_t* __restrict__ flags) {
+  __shared__ uint32_t red[1024];
   uint32_t bad = 0;
   for (int i = threadIdx.x; i < K; i += blockDim.x) {
     const float v = lam[i];
-    bad |= (v >= 0x1p-32f && v <= 0x1p32f) ? 0u : kLamRangeBit;   // false for NaN too
+    if (!(v >= 0x1p-32f && v <= 0x1p32f)) {      // false for NaN too
+      bad |= kLamRangeBit;
+      continue;
+    }
+    const float r = rlam[i], rl = rlo[i];
+    for (int mnt = 128; mnt < 256; ++mnt) {
+      const float x = float(mnt) * 0x1p-7f;
+      if (fmaf(x, r, x * rl) != x / v) bad |= kDivSlowBit;
+    }
   }
   red[threadIdx.x] = bad;
   __syncthreads();
@@ -519,14 +574,15 @@ static int pick_waves(int K) {
 
 template <int FMT>
 static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
-                                          const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales,
+                                          const float* rlam, const float* rlo, const void* L1f, uint8_t* codes,
+                                          uint8_t* scales,
                                           int64_t rows_pad, uint16_t* Dout, float* part, int r_pad, int kr,
                                           int splits, const uint32_t* wflags, hipStream_t s) {
   const dim3 grid(unsigned(rows_pad / (16 * kActRowTiles)), unsigned(splits)), block(64 * kActRowTiles);
-  const size_t shm = size_t(kr) * (8 + 2 * r_pad);
+  const size_t shm = size_t(kr) * (12 + 2 * r_pad);
   const uint4* l1 = reinterpret_cast<const uint4*>(L1f);
 #define SVDQ_QA(R16)                                                                                      \
-  hipLaunchKernelGGL((quantize_act_kernel<FMT, R16>), grid, block, shm, s, X, rows, ld, K, lam, rlam, l1, \
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, R16>), grid, block, shm, s, X, rows, ld, K, lam, rlam, rlo, l1, \
                      codes, scales, rows_pad, Dout, part, r_pad, kr, wflags)
   switch (r_pad / 16) {
     case 0: SVDQ_QA(0); break;
@@ -543,20 +599,21 @@ static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64
 #undef SVDQ_QA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || r_pad == 0) return e;
-  const int64_t total = rows_pad * r_pad;
-  hipLaunchKernelGGL(reduce_down_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, part, splits,
+  const int64_t total = rows_pad * r_pad;   // a multiple of 4 (r_pad is a multiple of 32)
+  hipLaunchKernelGGL(reduce_down_kernel, dim3(unsigned((total / 4 + 255) / 256)), dim3(256), 0, s, part, splits,
                      rows_pad, r_pad, Dout);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
-                               const float* rlam, const void* L1f, uint8_t* codes, uint8_t* scales, int64_t rows_pad,
+                               const float* rlam, const float* rlo, const void* L1f, uint8_t* codes, uint8_t* scales,
+                               int64_t rows_pad,
                                uint16_t* Dout, float* part, int r_pad, int kr, int splits, const uint32_t* wflags,
                                hipStream_t s) {
   if (fmt == kFmtMXFP4)
-    return launch_quantize_act_fmt<kFmtMXFP4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
+    return launch_quantize_act_fmt<kFmtMXFP4>(X, rows, ld, K, lam, rlam, rlo, L1f, codes, scales, rows_pad, Dout, part,
                                               r_pad, kr, splits, wflags, s);
-  return launch_quantize_act_fmt<kFmtINT4>(X, rows, ld, K, lam, rlam, L1f, codes, scales, rows_pad, Dout, part,
+  return launch_quantize_act_fmt<kFmtINT4>(X, rows, ld, K, lam, rlam, rlo, L1f, codes, scales, rows_pad, Dout, part,
                                            r_pad, kr, splits, wflags, s);
 }
 
@@ -589,8 +646,9 @@ hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* 
   const int64_t n = wl.N_pad > K ? wl.N_pad : K;
   hipLaunchKernelGGL(pack_vec_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, lam, K, bias, N, wl.N_pad,
                      reinterpret_cast<float*>(blob + wl.lam), reinterpret_cast<float*>(blob + wl.rlam),
-                     reinterpret_cast<uint16_t*>(blob + wl.bias));
-  hipLaunchKernelGGL(check_lambda_kernel, dim3(1), dim3(256), 0, s, lam, K,
+                     reinterpret_cast<float*>(blob + wl.rlo), reinterpret_cast<uint16_t*>(blob + wl.bias));
+  hipLaunchKernelGGL(check_lambda_kernel, dim3(1), dim3(1024), 0, s, reinterpret_cast<const float*>(blob + wl.lam),
+                     reinterpret_cast<const float*>(blob + wl.rlam), reinterpret_cast<const float*>(blob + wl.rlo), K,
                      reinterpret_cast<uint32_t*>(blob + wl.flags));
   return hipGetLastError();
 }
