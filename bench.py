@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="before the timed region, copy MIB mebibytes device to device once (a plain copy of "
+                        "known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -113,6 +116,13 @@ def gpu_leg(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
