@@ -51,8 +51,12 @@ def layers_of(workload):
 
 
 def gemm_source_hash() -> str:
-    with open(os.path.join(ROOT, "w4a4_quantized_linear_amd", "csrc", "gemm.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the GEMM kernels are compiled from."""
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "common.h", "layout.h"):
+        with open(os.path.join(ROOT, "w4a4_quantized_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):

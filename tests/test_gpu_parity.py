@@ -111,6 +111,33 @@ def test_layer_elementwise(torch_dev, case):
     check_fp32_output(Yg.cpu().numpy(), Ly.gelu(Y_o), "GELU output")
 
 
+def test_gelu_epilogue_pointwise(torch_dev):
+    """The GEMM's GELU against the exact erf form, value by value: with R = 0,
+    rank 0 and lambda = 1 the output is GELU(b), so the bias carries the test
+    values (2032 points spread over [-12, 12], rounded to bf16, and special values)."""
+    torch, dev = torch_dev
+    K, N, M = 512, 2048, 8
+    spec, L = _medium_layer("qkv", "mxfp4", M, K, N, 0, 31)
+    vals = np.concatenate([np.linspace(-12.0, 12.0, N - 16),
+                           [0.0, -0.0, 1e-30, -1e-30, 5e-39, 3e38, -3e38, 40.0, -40.0, 0.5, -0.5,
+                            1.0, -1.0, 6.0, -6.0, 9.0]]).astype(np.float32)
+    assert vals.size == N
+    L["b"] = synth.bf16_bits_from_f32(vals)
+    L["R"] = np.zeros_like(L["R"])
+    L["lam"] = np.ones_like(L["lam"])
+    layer = sq.Layer("mxfp4", K, N, 0)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    Y = sq.gemm(layer, w, ws, M, sq.EPI_BIAS | sq.EPI_GELU | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    b = F.bf16_value(L["b"]).astype(np.float64)
+    want = Ly.gelu(b)
+    got = Y.cpu().numpy().astype(np.float64)
+    assert np.all(got == got[0]), "every row sees the same bias"
+    err = np.abs(got[0] - want)
+    assert np.all(err <= 1e-6 * np.maximum(1.0, np.abs(b))), f"max GELU error {err.max():.3e}"
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
 def test_edge_values_bit_exact(torch_dev, fmt):
     """Zero rows, signed zeros, subnormal inputs after smoothing, huge values:
