@@ -125,6 +125,27 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* d, const void* w_packed, co
 svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void* a_packed,
                       int64_t M, void* Y, int64_t ldy, uint32_t epi, void* stream);
 
+/* Fused MLP step: launch 2 of layer d, whose output feeds layer dn (dn->K == d->N),
+ * with that output quantized for dn instead of stored.  The Nunchaku in Diffusers
+ * page (section "Background: SVDQuant and Nunchaku") names fused GELU/MLP kernels
+ * among the original engine's model-specific paths; this is that fusion for the
+ * 4-bit layer.  The epilogue forms H = bf16(act(acc + (X_hat L1) L2 + b)) exactly
+ * as svdq_gemm would store it, then smooths, quantizes and packs H for dn into
+ * an_packed as svdq_quantize_act(dn, wn_packed, H, M, ...) would: the same codes
+ * and scales bit for bit, and D' = H_hat L1' summed in a different (fixed) order
+ * (one fp32 partial per 256 columns of H, added in column order by a second
+ * launch).  svdq_gemm(dn, wn_packed, an_packed, ...) then completes dn.  H itself
+ * is never written.
+ *   d, w_packed, a_packed  layer d as for svdq_gemm (a_packed from svdq_quantize_act)
+ *   epi       SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU (no SVDQ_EPI_OUT_F32)
+ *   dn, wn_packed  the next layer and its packed weights
+ *   an_packed device, svdq_act_bytes(dn, M) bytes, 256-byte aligned
+ * Both layers MXFP4 (else SVDQ_ERR_FORMAT); dn->K != d->N or dn->rank > 64 give
+ * SVDQ_ERR_SHAPE; other checks and errors as svdq_gemm. */
+svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M,
+                            uint32_t epi, const svdq_layer_desc* dn, const void* wn_packed, void* an_packed,
+                            void* stream);
+
 /* Both launches; workspace >= svdq_act_bytes(d, M) bytes (device, 256-aligned). */
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
                         int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi,

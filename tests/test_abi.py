@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 100
+    assert L.svdq_version() == 101
     for s in range(8):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -114,6 +114,24 @@ def test_gemm_and_linear_validation(L, forced_device_error):
     assert lin(d, P, P, 4, 1024, P, 512, 3, P, need - 1, None) == 5
     assert lin(d, P, P, 4, 1024, P, 512, 3, P, need, None) == 6
     assert lin(d, P, P, 4, 1024, P, 512, 3, None, need, None) == 1
+
+
+def test_gemm_quant_validation(L, forced_device_error):
+    q = L.svdq_gemm_quant
+    d = ctypes.byref(D(K=1024, N=512, rank=16))          # this layer: 1024 -> 512
+    dn = ctypes.byref(D(K=512, N=256, rank=32))          # next layer: 512 -> 256
+    assert q(None, P, P, 4, 7, dn, P, P, None) == 1
+    assert q(d, P, P, 4, 7, None, P, P, None) == 1
+    assert q(d, P, P, 4, 7, dn, P, None, None) == 1
+    assert q(d, P, P, 4, 7, ctypes.byref(D(K=1024, N=256)), P, P, None) == 2      # next K != N
+    assert q(d, P, P, 4, 7, ctypes.byref(D(K=512, N=256, rank=80)), P, P, None) == 2  # next rank > 64
+    assert q(d, P, P, -1, 7, dn, P, P, None) == 2
+    assert q(ctypes.byref(D(fmt=2, K=1024, N=512)), P, P, 4, 7, dn, P, P, None) == 3   # INT4 not fused
+    assert q(d, P, P, 4, 7, ctypes.byref(D(fmt=2, K=512, N=256)), P, P, None) == 3
+    assert q(d, P, P, 4, 15, dn, P, P, None) == 3        # fp32 output flag
+    assert q(d, P, P, 4, 7, dn, P, P + 16, None) == 4    # workspace not 256-aligned
+    assert q(d, P, P, 4, 7, dn, P, P, None) == 6         # valid -> device check
+    assert q(d, P, P, 0, 7, dn, P, P, None) == 6
 
 
 def test_unpack_validation(L, forced_device_error):

@@ -1,0 +1,121 @@
+"""Fused MLP step (svdq_gemm_quant): the first layer's GEMM quantizes its bf16
+output H for the next layer instead of storing it.
+
+Checked against the unfused path on the same GPU inputs: svdq_gemm writes H,
+svdq_quantize_act quantizes it, and the fused call must leave the next layer's
+workspace with the same codes and scales bit for bit, and a down projection
+within the rounding bound of two fp32 sums of the same bf16 products.  Through
+the next layer's GEMM the fused chain is also checked against the oracle's
+chain (each side quantizes its own H), as the unfused chain is."""
+import numpy as np
+import pytest
+
+import synth
+import w4a4_quantized_linear_amd as sq
+from oracle import formats as F
+from oracle import layer as Ly
+
+from _gpu_helpers import bf16_to_np, check_chain_output, dev_tensor, pack
+
+pytestmark = pytest.mark.gpu
+
+EPI1 = sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU
+EPI2 = sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32
+
+# (M, K1, N1 = K2, rank1, N2, rank2, seed): ragged M, several 256-column tiles of
+# H, next-layer ranks 0 / 16 / 32 / 48, one row
+CASES = [
+    (300, 1024, 1024, 16, 512, 32, 1),
+    (513, 512, 2048, 32, 256, 48, 2),
+    (64, 1024, 512, 0, 1024, 0, 3),
+    (1, 512, 512, 32, 512, 16, 4),
+]
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sq.lib()
+    assert sq.device_check(), "current device is not gfx950"
+    return torch, torch.device("cuda:0")
+
+
+def _pair(M, K1, N1, r1, N2, r2, seed):
+    s1 = synth.layer_spec("fc1_mxfp4", M=M, K=K1, N=N1, rank=r1, x_outliers=max(1, K1 // 100),
+                          w_outliers=max(1, K1 // 100), lora_rank=0)
+    s2 = synth.layer_spec("fc2_mxfp4", M=M, K=N1, N=N2, rank=r2, x_outliers=0, w_outliers=max(1, N1 // 100),
+                          lora_rank=0)
+    return synth.draw_layer(s1, seed=seed), synth.draw_layer(s2, seed=seed + 100)
+
+
+def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2):
+    l1, l2 = sq.Layer("mxfp4", K1, N1, r1), sq.Layer("mxfp4", N1, N2, r2)
+    w1, w2 = pack(l1, L1, torch, dev), pack(l2, L2, torch, dev)
+    a1 = sq.quantize_act(l1, w1, dev_tensor(L1["X"], torch, dev))
+    print(f"fused pair M={M} {K1}->{N1}->{N2} ranks {r1}/{r2}", flush=True)
+    H = sq.gemm(l1, w1, a1, M, EPI1)
+    a2u = sq.quantize_act(l2, w2, H.view(torch.int16))
+    a2f = sq.gemm_quant(l1, w1, a1, M, EPI1, l2, w2)
+    uu, uf = sq.unpack_act(l2, a2u, M), sq.unpack_act(l2, a2f, M)
+    Y2u = sq.gemm(l2, w2, a2u, M, EPI2)
+    Y2f = sq.gemm(l2, w2, a2f, M, EPI2)
+    torch.cuda.synchronize()
+    return dict(H=H, uu=uu, uf=uf, Y2u=Y2u, Y2f=Y2f)
+
+
+def _check_against_unfused(torch, r, L2, r2, what):
+    uu, uf = r["uu"], r["uf"]
+    assert torch.equal(uu["codes"], uf["codes"]), f"{what}: codes differ from quantize_act(H)"
+    assert torch.equal(uu["scales"], uf["scales"]), f"{what}: scales differ from quantize_act(H)"
+    if r2:
+        # both are fp32 sums of the bf16 hi + lo products of x_hat with L1', each within
+        # 2^-14 of the exact sum relative to sum |x_hat| |L1'|
+        h = bf16_to_np(r["H"]).astype(np.float32)
+        xhat = (h / L2["lam"].astype(np.float32)).astype(np.float64)
+        bound = np.abs(xhat) @ np.abs(F.bf16_value(L2["L1"]))
+        diff = np.abs(uf["D"].cpu().numpy().astype(np.float64) - uu["D"].cpu().numpy().astype(np.float64))
+        assert np.all(diff <= 2.0 ** -13 * bound + 1e-30), f"{what}: down projection"
+    yu = r["Y2u"].cpu().numpy().astype(np.float64)
+    yf = r["Y2f"].cpu().numpy().astype(np.float64)
+    rms = float(np.sqrt(np.mean(yu ** 2)))
+    assert np.abs(yf - yu).max() <= 1e-4 * rms, f"{what}: next layer's output moved by {np.abs(yf - yu).max():.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"M{c[0]}-{c[1]}-{c[2]}-{c[4]}-r{c[3]}-{c[5]}" for c in CASES])
+def test_fused_equals_unfused_and_oracle_chain(torch_dev, case):
+    torch, dev = torch_dev
+    M, K1, N1, r1, N2, r2, seed = case
+    L1, L2 = _pair(*case)
+    r = _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2)
+    _check_against_unfused(torch, r, L2, r2, f"case {case}")
+    # the chain through the oracle, which forms and quantizes its own H
+    Y1_o = Ly.forward(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"], "mxfp4", gelu_act=True)["Y"]
+    Y2_o = Ly.forward(F.bf16_bits(Y1_o), L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], "mxfp4")["Y"]
+    check_chain_output(r["Y2f"].cpu().numpy(), Y2_o, "fused MLP output")
+
+
+def test_fused_ieee_division_path(torch_dev):
+    """A next-layer lambda outside [2^-32, 2^32] sends the whole layer to IEEE
+    division; the fused codes still equal quantize_act's."""
+    torch, dev = torch_dev
+    case = (200, 512, 1024, 16, 256, 32, 5)
+    L1, L2 = _pair(*case)
+    lam = L2["lam"].copy()
+    lam[3] = np.float32(2.0 ** 40)
+    lam[700] = np.float32(2.0 ** -35)
+    L2["lam"] = lam
+    r = _run(torch, dev, L1, L2, *case[:6])
+    _check_against_unfused(torch, r, L2, case[5], "lambda outside the fast range")
+
+
+def test_fused_full_size_flux_mlp(torch_dev):
+    """The FLUX MLP pair at its real size (fc1 4608 x 3072 -> 12288, GELU; fc2
+    12288 -> 3072; rank 32), as the benchmark's fused step runs it: codes and
+    scales of every row equal quantize_act's, D and fc2's output within bounds."""
+    torch, dev = torch_dev
+    s1, s2 = synth.CONFIGS["fc1_mxfp4"], synth.CONFIGS["fc2_mxfp4"]
+    L1, L2 = synth.draw_layer(s1), synth.draw_layer(s2)
+    r = _run(torch, dev, L1, L2, s1.M, s1.K, s1.N, s1.rank, s2.N, s2.rank)
+    _check_against_unfused(torch, r, L2, s2.rank, "FLUX MLP pair")

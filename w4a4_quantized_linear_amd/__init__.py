@@ -104,6 +104,20 @@ def gemm(layer: Layer, w_packed, a_packed, M: int, epi: int, out=None, stream=No
     return out
 
 
+def gemm_quant(layer: Layer, w_packed, a_packed, M: int, epi: int, next_layer: Layer, wn_packed, out=None,
+               stream=None):
+    """Launch 2 of `layer` with its bf16 output quantized for `next_layer` (fused MLP
+    step): returns next_layer's activation workspace, as quantize_act would fill it."""
+    d, p = _desc_ref(layer)
+    dn, pn = _desc_ref(next_layer)
+    if out is None:
+        out = _empty_u8(lib().svdq_act_bytes(pn, M), w_packed.device)
+    st = lib().svdq_gemm_quant(p, _ptr(w_packed), _ptr(a_packed), M, epi, pn, _ptr(wn_packed), _ptr(out),
+                               _stream(stream))
+    check("svdq_gemm_quant", st)
+    return out
+
+
 def linear(layer: Layer, w_packed, X, epi: int, out=None, workspace=None, stream=None):
     """Both launches: Y = act(deQ(Q(X/lam)) deQ(Q(R))^T + (X/lam L1) L2 + b)."""
     torch = _torch()

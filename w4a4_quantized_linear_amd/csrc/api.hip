@@ -20,6 +20,9 @@ hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* 
                            int N, int rank, const WeightLayout& wl, uint8_t* blob, hipStream_t s);
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s);
+hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
+                             int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
+                             uint8_t* nact, const ActLayout& nal, hipStream_t s);
 hipError_t launch_unpack_weight(int fmt, int K, int N, int rank, const WeightLayout& wl, const uint8_t* blob,
                                 uint8_t* codes, void* scales, uint16_t* L1, uint16_t* L2, float* lam, uint16_t* bias,
                                 hipStream_t s);
@@ -32,6 +35,7 @@ using namespace svdq;
 namespace {
 
 constexpr int64_t kMaxRows = int64_t(1) << 26;
+constexpr int kGemmQuantMaxRank = 64;   // next layer's rank in svdq_gemm_quant (4 rank tiles of 16)
 constexpr uint32_t kEpiAll = SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU | SVDQ_EPI_OUT_F32;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -98,7 +102,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 100; }
+int svdq_version(void) { return 101; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -178,6 +182,29 @@ svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void
   const ActLayout al = act_layout(d->K, d->rank, M);
   return launched(launch_gemm(d->fmt, static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                               al, d->K, d->N, M, Y, ldy, epi, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M,
+                            uint32_t epi, const svdq_layer_desc* dn, const void* wn_packed, void* an_packed,
+                            void* stream) {
+  if (!d || !dn || !w_packed || !a_packed || !wn_packed || !an_packed) return SVDQ_ERR_NULL;
+  svdq_status s = check_shape(d);
+  if (s != SVDQ_OK || (s = check_shape(dn)) != SVDQ_OK) return s;
+  if (M < 0 || M > kMaxRows || dn->K != d->N || dn->rank > kGemmQuantMaxRank) return SVDQ_ERR_SHAPE;
+  if ((s = check_fmt(d)) != SVDQ_OK || (s = check_fmt(dn)) != SVDQ_OK) return s;
+  if (d->fmt != SVDQ_MXFP4 || dn->fmt != SVDQ_MXFP4) return SVDQ_ERR_FORMAT;
+  if ((epi & ~(SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU)) != 0) return SVDQ_ERR_FORMAT;
+  if (!aligned(w_packed, 256) || !aligned(a_packed, 256) || !aligned(wn_packed, 256) || !aligned(an_packed, 256))
+    return SVDQ_ERR_ALIGN;
+  if ((s = device_check()) != SVDQ_OK) return s;
+  if (M == 0) return SVDQ_OK;
+  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->K, d->rank, M);
+  const WeightLayout nwl = weight_layout(dn->K, dn->N, dn->rank);
+  const ActLayout nal = act_layout(dn->K, dn->rank, M);
+  return launched(launch_gemm_quant(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
+                                    al, d->K, d->N, M, epi, static_cast<const uint8_t*>(wn_packed), nwl,
+                                    static_cast<uint8_t*>(an_packed), nal, static_cast<hipStream_t>(stream)));
 }
 
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M, int64_t ldx,

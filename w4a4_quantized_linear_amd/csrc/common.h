@@ -100,6 +100,30 @@ __device__ __forceinline__ void unpack_i4x8(uint32_t d, int& even, int& odd) {
   odd = int(((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
 }
 
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one row's group)
+__device__ __forceinline__ float rowgroup_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const uint32_t ua = __float_as_uint(a);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(ua, ua, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// True when some of the 16 bf16 values has a biased exponent outside
+// [87, 187), i.e. |x| outside [2^-40, 2^60) (zeros and subnormals included):
+// per 16-bit half, ((bits & 0x7F80) - 0x2B80) mod 2^16 > 0x3180.
+__device__ __forceinline__ bool exp_out_of_range(const uint4& a, const uint4& b) {
+  const u16x2 lo = {0x2B80, 0x2B80};
+  auto f = [&](uint32_t v) { return __builtin_bit_cast(u16x2, v & 0x7F807F80u) - lo; };
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_elementwise_max(f(a.x), f(a.y)), __builtin_elementwise_max(f(a.z), f(a.w))),
+      __builtin_elementwise_max(__builtin_elementwise_max(f(b.x), f(b.y)), __builtin_elementwise_max(f(b.z), f(b.w))));
+  return (m.x > m.y ? m.x : m.y) > 0x3180;
+}
+
 // GELU in the erf form, y * Phi(y) = (y + |y| erf(|y| / sqrt 2)) / 2, with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.28:
 //   erf(z) = 1 - 1 / (1 + a1 z + a2 z^2 + ... + a6 z^6)^16,  z >= 0, absolute error <= 3e-7.

@@ -18,6 +18,8 @@
 // then int32 -> fp32 times sW * sX accumulated in fp32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "svdq.h"
 #include "common.h"
 
@@ -32,6 +34,14 @@ struct GemmArgs {
   int K, N, r_pad;
   uint32_t epi;
   void* Y;
+  // Output quantized for the next layer instead of Y (its K is N): that layer's
+  // packed weights (lambda, 1/lambda, the correction, L1, flags) and activation
+  // workspace (codes, scales, down-projection partials).
+  const uint8_t* nblob;
+  uint8_t* nact;
+  size_t n_lam, n_rlam, n_rlo, n_L1, n_flags;
+  size_t n_codes, n_scales, n_part;
+  int nr_pad;
 };
 
 // ------------------------------------------------------------------ epilogue pieces
@@ -138,6 +148,189 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM],
   }
 }
 
+// Output quantized for the next layer (the fused MLP step: the next row after
+// the layer itself; the Nunchaku in Diffusers page, section "Background:
+// SVDQuant and Nunchaku", names fused GELU/MLP kernels among the original
+// engine's model-specific paths).  H = bf16(act(acc + b)) is the next layer's
+// input X (its K is this layer's N).  Instead of storing H, each value is
+// smoothed by that layer's lambda and quantized to MXFP4 exactly as the
+// activation kernel would do with H read from memory (same rounding of H, same
+// quotients, same group maxima and codes), and the wave's share of the next
+// layer's down projection H_hat L1' goes to an fp32 partial per 256-column tile
+// of this layer (summed in tile order by a second launch).
+//
+// A wave's 128 columns n0 .. n0+127 are one 128-K step of the next layer, i.e.
+// 4 blocks of 32 (fragments 2b, 2b+1); a row's 32 values of block b sit in the
+// lanes r, r+16, r+32, r+48 (r = row % 16), 4 per fragment.  For the down
+// projection the lane's 8 values of block b (k = 4q + t of fragment 2b, then of
+// 2b+1; q = lane / 16) are one bf16 MFMA A operand, and L1' is gathered in the
+// same K order, so each 32-K product is the block's dot product.
+template <int WN, int WM, bool GELU>
+__device__ __forceinline__ void store_quant(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
+                                            int64_t n0, int64_t m0, int lane, int wn, int wm, int tn,
+                                            uint8_t* stage, v4f* dred) {
+  static_assert(WN == 8, "a wave's 128 columns are one 128-K step of the next layer");
+  const int q = lane >> 4, r = lane & 15;
+  const int K2 = g.N;
+  const int ks = int(n0 / kKStep);
+  const float* nlam = reinterpret_cast<const float*>(g.nblob + g.n_lam) + n0;
+  const uint32_t wf = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(g.nblob + g.n_flags));
+  const bool ieee_only = (wf & kLamRangeBit) != 0;
+  const bool div2 = (wf & kDivSlowBit) == 0;
+  // 1/lambda and the correction term of the lane's 32 columns n0 + 16 i + 4 q + e
+  float rv[WN][4], rlv[WN][4];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.nblob + g.n_rlam) + n0 + 16 * i + 4 * q);
+    const float4 c = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.nblob + g.n_rlo) + n0 + 16 * i + 4 * q);
+    rv[i][0] = a.x; rv[i][1] = a.y; rv[i][2] = a.z; rv[i][3] = a.w;
+    rlv[i][0] = c.x; rlv[i][1] = c.y; rlv[i][2] = c.z; rlv[i][3] = c.w;
+  }
+  // L1' B operands of the wave's 4 blocks and rank tiles c (rank column c * 16 + r),
+  // gathered from the stored fragments (lane L holds k = (L / 16) * 8 .. + 7).
+  constexpr int kMaxR16 = 4;
+  const int R16 = g.nr_pad / 16;
+  uint4 l1g[4][kMaxR16];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int c = 0; c < kMaxR16; ++c) {
+      l1g[b][c] = uint4{0u, 0u, 0u, 0u};
+      if (c < R16) {
+        const uint8_t* t = g.nblob + g.n_L1 + ((size_t(n0 / 32 + b) * R16 + c) * 64) * 16 + (q & 1) * 8;
+        const uint2 lo = *reinterpret_cast<const uint2*>(t + ((q >> 1) * 16 + r) * 16);
+        const uint2 hi = *reinterpret_cast<const uint2*>(t + ((2 + (q >> 1)) * 16 + r) * 16);
+        l1g[b][c] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+  uint8_t* const codes = g.nact + g.n_codes;
+  uint8_t* const scales = g.nact + g.n_scales;
+  float* const part = reinterpret_cast<float*>(g.nact + g.n_part);
+
+  // One 16-row tile j of the wave (a compile-time index, so acc stays in registers;
+  // the body is too large for the loop unroller).
+  auto row_tile = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    // H in bf16, exactly as the bf16 output of this layer would hold it
+    uint32_t hb[WN][2];
+    float h[WN][4];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = acc[i][j][e] + bv[i][e];
+        if (GELU) y[e] = gelu_erf(y[e]);
+      }
+      hb[i][0] = pack_bf2(y[0], y[1]);
+      hb[i][1] = pack_bf2(y[2], y[3]);
+      h[i][0] = bf_lo(hb[i][0]); h[i][1] = bf_hi(hb[i][0]);
+      h[i][2] = bf_lo(hb[i][1]); h[i][3] = bf_hi(hb[i][1]);
+    }
+    // smoothing divide: the activation kernel's three paths, same quotients
+    const bool oor = exp_out_of_range(uint4{hb[0][0], hb[0][1], hb[1][0], hb[1][1]},
+                                      uint4{hb[2][0], hb[2][1], hb[3][0], hb[3][1]}) ||
+                     exp_out_of_range(uint4{hb[4][0], hb[4][1], hb[5][0], hb[5][1]},
+                                      uint4{hb[6][0], hb[6][1], hb[7][0], hb[7][1]});
+    const bool fast = !ieee_only && !__any(oor);
+    float x[WN][4];
+    if (__builtin_expect(fast && div2, 1)) {
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i][e] = fmaf(h[i][e], rv[i][e], h[i][e] * rlv[i][e]);
+    } else if (fast) {
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i][e] = div_refined(h[i][e], nlam[16 * i + 4 * q + e], rv[i][e]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i][e] = h[i][e] / nlam[16 * i + 4 * q + e];
+    }
+    // per block: group maximum over the row's 4 lanes, E8M0 scale, E2M1 codes
+    const int64_t mrow = m0 + 16 * j + r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(x[2 * b][e]), fabsf(x[2 * b + 1][e])));
+      amax = rowgroup_max(amax);
+      const uint32_t sb = e8m0_of_amax(amax);
+      const float inv = inv_scale_of_e8m0(sb);
+      uint32_t cw = 0;
+      cw = cvt_fp4x2<0>(cw, x[2 * b][0] * inv, x[2 * b][1] * inv);
+      cw = cvt_fp4x2<1>(cw, x[2 * b][2] * inv, x[2 * b][3] * inv);
+      cw = cvt_fp4x2<2>(cw, x[2 * b + 1][0] * inv, x[2 * b + 1][1] * inv);
+      cw = cvt_fp4x2<3>(cw, x[2 * b + 1][2] * inv, x[2 * b + 1][3] * inv);
+      // lane chunk r + 16 b of the 16-row tile: elements 4q .. 4q+3 in bytes 2q, 2q+1,
+      // elements 16 + 4q .. in bytes 8 + 2q, 9 + 2q
+      uint8_t* chunk = stage + (r + 16 * b) * 16;
+      *reinterpret_cast<uint16_t*>(chunk + 2 * q) = uint16_t(cw);
+      *reinterpret_cast<uint16_t*>(chunk + 8 + 2 * q) = uint16_t(cw >> 16);
+      if (q == b) scales[mx_scale_byte(mrow, ks * 4 + b, K2)] = uint8_t(sb);
+    }
+    *reinterpret_cast<uint4*>(codes + code_chunk((m0 + 16 * j) / 16, ks, K2, lane)) =
+        *reinterpret_cast<const uint4*>(stage + lane * 16);
+    // down projection of the wave's 128 K: x_hat as bf16 hi + lo against L1'
+    if (R16 > 0) {
+      v4f d[kMaxR16];
+#pragma unroll
+      for (int c = 0; c < kMaxR16; ++c) d[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint4 hi, lo;
+        hi.x = cvt_bf2(x[2 * b][0], x[2 * b][1]);
+        hi.y = cvt_bf2(x[2 * b][2], x[2 * b][3]);
+        hi.z = cvt_bf2(x[2 * b + 1][0], x[2 * b + 1][1]);
+        hi.w = cvt_bf2(x[2 * b + 1][2], x[2 * b + 1][3]);
+        lo.x = cvt_bf2(x[2 * b][0] - bf_lo(hi.x), x[2 * b][1] - bf_hi(hi.x));
+        lo.y = cvt_bf2(x[2 * b][2] - bf_lo(hi.y), x[2 * b][3] - bf_hi(hi.y));
+        lo.z = cvt_bf2(x[2 * b + 1][0] - bf_lo(hi.z), x[2 * b + 1][1] - bf_hi(hi.z));
+        lo.w = cvt_bf2(x[2 * b + 1][2] - bf_lo(hi.w), x[2 * b + 1][3] - bf_hi(hi.w));
+#pragma unroll
+        for (int c = 0; c < kMaxR16; ++c)
+          if (c < R16) {
+            d[c] = mfma_bf16(hi, l1g[b][c], d[c]);
+            d[c] = mfma_bf16(lo, l1g[b][c], d[c]);
+          }
+      }
+      // the two waves of a row range (wn = 0, 1) add their halves in LDS, in that
+      // order; wave wn = 0 writes the workgroup's partial of N tile tn
+      v4f* dr = dred + ((wm * 2 + (j & 1)) * kMaxR16) * 64 + lane;
+      if (wn == 1) {
+#pragma unroll
+        for (int c = 0; c < kMaxR16; ++c)
+          if (c < R16) dr[c * 64] = d[c];
+      }
+      __syncthreads();
+      if (wn == 0) {
+#pragma unroll
+        for (int c = 0; c < kMaxR16; ++c)
+          if (c < R16) {
+            const v4f o = dr[c * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t mm = m0 + 16 * j + (lane >> 4) * 4 + e;
+              part[(size_t(tn) * g.M_pad + mm) * g.nr_pad + c * 16 + r] = d[c][e] + o[e];
+            }
+          }
+      }
+    }
+  };
+  static_assert(WM == 8, "eight 16-row tiles per wave");
+  row_tile(std::integral_constant<int, 0>{});
+  row_tile(std::integral_constant<int, 1>{});
+  row_tile(std::integral_constant<int, 2>{});
+  row_tile(std::integral_constant<int, 3>{});
+  row_tile(std::integral_constant<int, 4>{});
+  row_tile(std::integral_constant<int, 5>{});
+  row_tile(std::integral_constant<int, 6>{});
+  row_tile(std::integral_constant<int, 7>{});
+}
+
 // Whole epilogue after the main loop: low-rank MFMAs first (their operand loads
 // come before any store), then every bias value, then bias + activation +
 // conversion + stores with no loads in between (the vector-memory counter also
@@ -199,7 +392,7 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WN, int WM, bool OUT_F32, bool GELU>
+template <int WN, int WM, bool OUT_F32, bool GELU, bool QOUT = false>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   __shared__ uint4 ring0[kStageU4], ring1[kStageU4], ring2[kStageU4], ring3[kStageU4];   // 4 x 32 KiB
   static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
@@ -325,7 +518,15 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
 #undef SVDQ_FP4_STEP
   // every wave passed the last barrier with no load in flight: the ring is free
   // for the output staging (one slot per wave)
-  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+  if constexpr (QOUT) {
+    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    float bv[WN][4];
+    load_bias<WN>(g, n0, lane, bv);
+    store_quant<WN, WM, GELU>(g, acc, bv, n0, m0, lane, wn, wm, tn, reinterpret_cast<uint8_t*>(ring0) + w * 1024,
+                              reinterpret_cast<v4f*>(ring1));
+  } else {
+    epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+  }
 }
 
 // ------------------------------------------------------------------ INT4
@@ -434,6 +635,38 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
   }
 #undef SVDQ_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_reduce_down(const float* part, int splits, int64_t rows_pad, int r_pad, uint16_t* Dout, hipStream_t s);
+
+// The GEMM of one layer with its bf16 output quantized for the next layer (MXFP4
+// both), then the sum of the down-projection partials into that layer's D.
+hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
+                             int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
+                             uint8_t* nact, const ActLayout& nal, hipStream_t s) {
+  GemmArgs g{};
+  g.wblob = wblob;
+  g.act = act;
+  g.w_codes = wl.codes; g.w_scales = wl.scales; g.w_L2 = wl.L2; g.w_bias = wl.bias;
+  g.a_codes = al.codes; g.a_scales = al.scales; g.a_D = al.D;
+  g.N_pad = wl.N_pad; g.M_pad = al.M_pad; g.M = M; g.ldy = 0;
+  g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
+  g.epi = epi;
+  g.Y = nullptr;
+  g.nblob = nblob;
+  g.nact = nact;
+  g.n_lam = nwl.lam; g.n_rlam = nwl.rlam; g.n_rlo = nwl.rlo; g.n_L1 = nwl.L1; g.n_flags = nwl.flags;
+  g.n_codes = nal.codes; g.n_scales = nal.scales; g.n_part = nal.part;
+  g.nr_pad = int(nwl.r_pad);
+  const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+  if (epi & SVDQ_EPI_GELU)
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, true>), dim3(nb), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, true>), dim3(nb), dim3(256), 0, s, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nwl.r_pad == 0) return e;
+  return launch_reduce_down(reinterpret_cast<const float*>(nact + nal.part), N / kTileRows, nal.M_pad,
+                            int(nwl.r_pad), reinterpret_cast<uint16_t*>(nact + nal.D), s);
 }
 
 }  // namespace svdq

@@ -96,7 +96,10 @@ __host__ __device__ inline void act_split(int K, int r_pad, int64_t M_pad, int* 
 }
 
 // Codes: M_pad x K/2.  Scales: M_pad x K/32 bytes.  D: M_pad x r_pad x {hi, lo} bf16.
-// part: fp32 partial down projections, splits x M_pad x r_pad (only with splits > 1).
+// part: fp32 partial down projections, P x M_pad x r_pad, for the larger of the two
+// producers: the activation kernel's K splits (when it splits K), and the GEMM of a
+// previous layer that quantizes its output for this layer (one partial per 256
+// columns of that output, K / 256 of them).
 __host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
   ActLayout a;
   a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
@@ -106,7 +109,8 @@ __host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
   a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
   a.scales = o; o = align256(o + size_t(a.M_pad) * K / 32);
   a.D = o;      o = align256(o + size_t(a.M_pad) * a.r_pad * 4);
-  a.part = o;   o = align256(o + (a.splits > 1 ? size_t(a.splits) * a.M_pad * a.r_pad * 4 : 0));
+  const int nparts = (a.splits > 1 && a.splits > K / kTileRows) ? a.splits : K / kTileRows;
+  a.part = o;   o = align256(o + size_t(nparts) * a.M_pad * a.r_pad * 4);
   a.total = o;
   return a;
 }

@@ -122,30 +122,6 @@ __device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
   a[4] = bf_lo(r.z); a[5] = bf_hi(r.z); a[6] = bf_lo(r.w); a[7] = bf_hi(r.w);
 }
 
-// max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one row's group)
-__device__ __forceinline__ float rowgroup_max(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float a = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
-  const uint32_t ua = __float_as_uint(a);
-  const auto p32 = __builtin_amdgcn_permlane32_swap(ua, ua, false, false);
-  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
-}
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// True when some of the 16 bf16 values has a biased exponent outside
-// [87, 187), i.e. |x| outside [2^-40, 2^60) (zeros and subnormals included):
-// per 16-bit half, ((bits & 0x7F80) - 0x2B80) mod 2^16 > 0x3180.
-__device__ __forceinline__ bool exp_out_of_range(const uint4& a, const uint4& b) {
-  const u16x2 lo = {0x2B80, 0x2B80};
-  auto f = [&](uint32_t v) { return __builtin_bit_cast(u16x2, v & 0x7F807F80u) - lo; };
-  const u16x2 m = __builtin_elementwise_max(
-      __builtin_elementwise_max(__builtin_elementwise_max(f(a.x), f(a.y)), __builtin_elementwise_max(f(a.z), f(a.w))),
-      __builtin_elementwise_max(__builtin_elementwise_max(f(b.x), f(b.y)), __builtin_elementwise_max(f(b.z), f(b.w))));
-  return (m.x > m.y ? m.x : m.y) > 0x3180;
-}
-
 constexpr int kActStep = 64;   // K per pipeline step: two 32-blocks (one INT4 group)
 constexpr int kActDepth = 3;   // steps of X in flight ahead of the one being computed
 
@@ -572,6 +548,15 @@ static int pick_waves(int K) {
   return n < 8 ? n : 8;
 }
 
+// D = the sum of `splits` fp32 partials (splits x rows_pad x r_pad), in order, as bf16 hi + lo.
+hipError_t launch_reduce_down(const float* part, int splits, int64_t rows_pad, int r_pad, uint16_t* Dout,
+                              hipStream_t s) {
+  const int64_t total = rows_pad * r_pad;   // a multiple of 4 (r_pad is a multiple of 32)
+  hipLaunchKernelGGL(reduce_down_kernel, dim3(unsigned((total / 4 + 255) / 256)), dim3(256), 0, s, part, splits,
+                     rows_pad, r_pad, Dout);
+  return hipGetLastError();
+}
+
 template <int FMT>
 static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
                                           const float* rlam, const float* rlo, const void* L1f, uint8_t* codes,
@@ -599,10 +584,7 @@ static hipError_t launch_quantize_act_fmt(const uint16_t* X, int64_t rows, int64
 #undef SVDQ_QA
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || r_pad == 0) return e;
-  const int64_t total = rows_pad * r_pad;   // a multiple of 4 (r_pad is a multiple of 32)
-  hipLaunchKernelGGL(reduce_down_kernel, dim3(unsigned((total / 4 + 255) / 256)), dim3(256), 0, s, part, splits,
-                     rows_pad, r_pad, Dout);
-  return hipGetLastError();
+  return launch_reduce_down(part, splits, rows_pad, r_pad, Dout, s);
 }
 
 hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
