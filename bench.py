@@ -9,6 +9,9 @@ timing, as at load time).  value = (2 M N K of fc1 + of fc2) per step / time.
 Prints one JSON line.  `roofline` is the fc1 GEMM kernel (the dominant launch),
 timed with HIP events around each of its launches inside the timed region.
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+For the MXFP4 pair, `fused_mlp` times the same pair with fc1's GEMM quantizing
+its output for fc2 in its epilogue (svdq_gemm_quant: three launches plus the
+down-projection sum instead of four), same inputs, same step count.
 """
 from __future__ import annotations
 
@@ -167,8 +170,44 @@ def gpu_leg(args):
             "gemm_TFLOPs": round(flops[i] / (gemm_us[i] * 1e-6) / 1e12, 1),
             "linear_TOPS": round(flops[i] / ((gemm_us[i] + quant_us[i]) * 1e-6) / 1e12, 1),
         }
+    fused = None
+    if args.workload == "mlp_mxfp4":
+        fused = fused_pair(args, sq, torch, layers, weights, inputs[0], ws, outs, epis, M, sum(flops))
     return dict(value=value, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps, roofline=roofline,
-                breakdown=breakdown, specs=specs, fmt=specs[0].fmt)
+                breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused)
+
+
+def fused_pair(args, sq, torch, layers, weights, x, ws, outs, epis, M, flops):
+    """The MLP pair with fc1's output quantized for fc2 inside fc1's GEMM."""
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sq.quantize_act(layers[0], weights[0], x, out=ws[0])
+        if ev is not None:
+            ev[1].record()
+        sq.gemm_quant(layers[0], weights[0], ws[0], M, epis[0], layers[1], weights[1], out=ws[1])
+        if ev is not None:
+            ev[2].record()
+        sq.gemm(layers[1], weights[1], ws[1], M, epis[1], out=outs[1])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    seg = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) * 1e3 / args.steps
+           for i in range(3)]
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
+            "fc1_quantize_us": round(seg[0], 2), "fc1_gemm_quant_us": round(seg[1], 2),
+            "fc2_gemm_us": round(seg[2], 2),
+            "launches": "fc1 quantize_act; fc1 gemm_quant (GEMM + fc2 quantize in the epilogue, then the "
+                        "down-projection sum); fc2 gemm"}
 
 
 def cpu_baseline(specs, budget_rows=512):
@@ -226,6 +265,8 @@ def main():
         "config": cfg, "roofline": r["roofline"], "breakdown": r["breakdown"],
         "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4),
     }
+    if r["fused"] is not None:
+        line["fused_mlp"] = r["fused"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(specs)
     print(json.dumps(line), flush=True)

@@ -100,6 +100,12 @@ __device__ __forceinline__ void unpack_i4x8(uint32_t d, int& even, int& odd) {
   odd = int(((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
 }
 
+// 8 packed bf16 -> fp32, element order kept
+__device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
+  a[0] = bf_lo(r.x); a[1] = bf_hi(r.x); a[2] = bf_lo(r.y); a[3] = bf_hi(r.y);
+  a[4] = bf_lo(r.z); a[5] = bf_hi(r.z); a[6] = bf_lo(r.w); a[7] = bf_hi(r.w);
+}
+
 // max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one row's group)
 __device__ __forceinline__ float rowgroup_max(float v) {
   const uint32_t u = __float_as_uint(v);
@@ -112,12 +118,17 @@ __device__ __forceinline__ float rowgroup_max(float v) {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// True when some of the 16 bf16 values has a biased exponent outside
-// [87, 187), i.e. |x| outside [2^-40, 2^60) (zeros and subnormals included):
-// per 16-bit half, ((bits & 0x7F80) - 0x2B80) mod 2^16 > 0x3180.
+// True when some of the 16 bf16 values is outside the fast divisions' range:
+// a biased exponent outside [87, 187), i.e. |x| < 2^-40 or |x| >= 2^60
+// (subnormals and -0 included), except +0, which every path (two-operation,
+// refined, IEEE) divides to +0 by a positive divisor.  Per 16-bit half:
+// ((bits & 0x7F80) - 0x2B80) mod 2^16 > 0x3180, masked to 0 when bits == 0.
 __device__ __forceinline__ bool exp_out_of_range(const uint4& a, const uint4& b) {
-  const u16x2 lo = {0x2B80, 0x2B80};
-  auto f = [&](uint32_t v) { return __builtin_bit_cast(u16x2, v & 0x7F807F80u) - lo; };
+  const u16x2 lo = {0x2B80, 0x2B80}, one = {1, 1};
+  auto f = [&](uint32_t v) {
+    const u16x2 nz = __builtin_elementwise_min(__builtin_bit_cast(u16x2, v), one);
+    return (__builtin_bit_cast(u16x2, v & 0x7F807F80u) - lo) * nz;
+  };
   const u16x2 m = __builtin_elementwise_max(
       __builtin_elementwise_max(__builtin_elementwise_max(f(a.x), f(a.y)), __builtin_elementwise_max(f(a.z), f(a.w))),
       __builtin_elementwise_max(__builtin_elementwise_max(f(b.x), f(b.y)), __builtin_elementwise_max(f(b.z), f(b.w))));

@@ -152,68 +152,33 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM],
 // the layer itself; the Nunchaku in Diffusers page, section "Background:
 // SVDQuant and Nunchaku", names fused GELU/MLP kernels among the original
 // engine's model-specific paths).  H = bf16(act(acc + b)) is the next layer's
-// input X (its K is this layer's N).  Instead of storing H, each value is
-// smoothed by that layer's lambda and quantized to MXFP4 exactly as the
-// activation kernel would do with H read from memory (same rounding of H, same
-// quotients, same group maxima and codes), and the wave's share of the next
-// layer's down projection H_hat L1' goes to an fp32 partial per 256-column tile
-// of this layer (summed in tile order by a second launch).
+// input X (its K is this layer's N).  Instead of storing H, the workgroup
+// quantizes its 256 x 256 tile of H for the next layer exactly as the
+// activation kernel does with H read from memory (same rounding of H, same
+// quotients, group maxima, scales and codes), and writes its tile's share of
+// the next layer's down projection H_hat L1' as one fp32 partial per 256
+// columns of H (summed in column order by a second launch).
 //
-// A wave's 128 columns n0 .. n0+127 are one 128-K step of the next layer, i.e.
-// 4 blocks of 32 (fragments 2b, 2b+1); a row's 32 values of block b sit in the
-// lanes r, r+16, r+32, r+48 (r = row % 16), 4 per fragment.  For the down
-// projection the lane's 8 values of block b (k = 4q + t of fragment 2b, then of
-// 2b+1; q = lane / 16) are one bf16 MFMA A operand, and L1' is gathered in the
-// same K order, so each 32-K product is the block's dot product.
-template <int WN, int WM, bool GELU>
-__device__ __forceinline__ void store_quant(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
-                                            int64_t n0, int64_t m0, int lane, int wn, int wm, int tn,
-                                            uint8_t* stage, v4f* dred) {
-  static_assert(WN == 8, "a wave's 128 columns are one 128-K step of the next layer");
-  const int q = lane >> 4, r = lane & 15;
-  const int K2 = g.N;
-  const int ks = int(n0 / kKStep);
-  const float* nlam = reinterpret_cast<const float*>(g.nblob + g.n_lam) + n0;
-  const uint32_t wf = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(g.nblob + g.n_flags));
-  const bool ieee_only = (wf & kLamRangeBit) != 0;
-  const bool div2 = (wf & kDivSlowBit) == 0;
-  // 1/lambda and the correction term of the lane's 32 columns n0 + 16 i + 4 q + e
-  float rv[WN][4], rlv[WN][4];
-#pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.nblob + g.n_rlam) + n0 + 16 * i + 4 * q);
-    const float4 c = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(g.nblob + g.n_rlo) + n0 + 16 * i + 4 * q);
-    rv[i][0] = a.x; rv[i][1] = a.y; rv[i][2] = a.z; rv[i][3] = a.w;
-    rlv[i][0] = c.x; rlv[i][1] = c.y; rlv[i][2] = c.z; rlv[i][3] = c.w;
-  }
-  // L1' B operands of the wave's 4 blocks and rank tiles c (rank column c * 16 + r),
-  // gathered from the stored fragments (lane L holds k = (L / 16) * 8 .. + 7).
-  constexpr int kMaxR16 = 4;
-  const int R16 = g.nr_pad / 16;
-  uint4 l1g[4][kMaxR16];
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int c = 0; c < kMaxR16; ++c) {
-      l1g[b][c] = uint4{0u, 0u, 0u, 0u};
-      if (c < R16) {
-        const uint8_t* t = g.nblob + g.n_L1 + ((size_t(n0 / 32 + b) * R16 + c) * 64) * 16 + (q & 1) * 8;
-        const uint2 lo = *reinterpret_cast<const uint2*>(t + ((q >> 1) * 16 + r) * 16);
-        const uint2 hi = *reinterpret_cast<const uint2*>(t + ((2 + (q >> 1)) * 16 + r) * 16);
-        l1g[b][c] = uint4{lo.x, lo.y, hi.x, hi.y};
-      }
-    }
-  uint8_t* const codes = g.nact + g.n_codes;
-  uint8_t* const scales = g.nact + g.n_scales;
-  float* const part = reinterpret_cast<float*>(g.nact + g.n_part);
+// Phase 1: each wave writes its 128 x 128 block of H (bf16) into LDS, the
+// workgroup's 256 rows x 256 columns in the four ring slots (64 rows each,
+// 512 bytes per row, 16-byte chunks swizzled by the row against bank
+// conflicts).  Phase 2: wave w quantizes rows 64 w .. 64 w + 63 from LDS in the
+// activation kernel's lane layout (lane = row % 16 + 16 c holds 8 consecutive
+// elements of each 32-block), 64 columns per step.
 
-  // One 16-row tile j of the wave (a compile-time index, so acc stays in registers;
-  // the body is too large for the loop unroller).
-  auto row_tile = [&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    // H in bf16, exactly as the bf16 output of this layer would hold it
-    uint32_t hb[WN][2];
-    float h[WN][4];
+// Byte offset of bf16 element (row % 64, column k) of the tile in its slot.
+__device__ __forceinline__ uint32_t htile_off(int row, int k) {
+  return uint32_t((row & 63) * 512 + (((k >> 3) ^ (row & 31)) << 4) + (k & 7) * 2);
+}
+
+template <int WN, int WM, bool GELU>
+__device__ __forceinline__ void stage_h(v4f (&acc)[WN][WM], const float (&bv)[WN][4], int lane, int wn, int wm,
+                                        uint8_t* lo0, uint8_t* lo1, uint8_t* hi0, uint8_t* hi1) {
+  const int q = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int row = wm * 128 + j * 16 + r;           // row within the workgroup tile
+    uint8_t* const sl = wm == 0 ? (j < 4 ? lo0 : lo1) : (j < 4 ? hi0 : hi1);   // slot (row / 64)
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       float y[4];
@@ -222,113 +187,129 @@ __device__ __forceinline__ void store_quant(const GemmArgs& g, v4f (&acc)[WN][WM
         y[e] = acc[i][j][e] + bv[i][e];
         if (GELU) y[e] = gelu_erf(y[e]);
       }
-      hb[i][0] = pack_bf2(y[0], y[1]);
-      hb[i][1] = pack_bf2(y[2], y[3]);
-      h[i][0] = bf_lo(hb[i][0]); h[i][1] = bf_hi(hb[i][0]);
-      h[i][2] = bf_lo(hb[i][1]); h[i][3] = bf_hi(hb[i][1]);
+      *reinterpret_cast<uint2*>(sl + htile_off(row, wn * 128 + i * 16 + q * 4)) =
+          make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
     }
-    // smoothing divide: the activation kernel's three paths, same quotients
-    const bool oor = exp_out_of_range(uint4{hb[0][0], hb[0][1], hb[1][0], hb[1][1]},
-                                      uint4{hb[2][0], hb[2][1], hb[3][0], hb[3][1]}) ||
-                     exp_out_of_range(uint4{hb[4][0], hb[4][1], hb[5][0], hb[5][1]},
-                                      uint4{hb[6][0], hb[6][1], hb[7][0], hb[7][1]});
-    const bool fast = !ieee_only && !__any(oor);
-    float x[WN][4];
-    if (__builtin_expect(fast && div2, 1)) {
+  }
+}
+
+// The next layer's L1' fragments (B operands of its down projection) for the
+// tile's 8 32-blocks and R16 rank tiles, into registers ahead of phase 2 (so
+// that no global load, which would also wait for the stores before it, sits
+// inside phase 2).
+template <int R16>
+__device__ __forceinline__ void load_l1_next(const GemmArgs& g, int k0, int lane, uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+  const uint4* const l1f = reinterpret_cast<const uint4*>(g.nblob + g.n_L1);
 #pragma unroll
-      for (int i = 0; i < WN; ++i)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[i][e] = fmaf(h[i][e], rv[i][e], h[i][e] * rlv[i][e]);
-    } else if (fast) {
+    for (int cb = 0; cb < R16; ++cb) l1r[kb][cb] = l1f[(size_t(k0 / 32 + kb) * R16 + cb) * 64 + lane];
+}
+
+// Phase 2 loop for wave w: rows mrow0 .. mrow0 + 63 of the tile (slot w).  lamv
+// holds lambda, 1/lambda and the correction term of the tile's 256 columns
+// (the next layer's K range k0 .. k0 + 255).  FAST: every quotient by the
+// two-operation form fma(x, r, x rl); otherwise by IEEE division.  Both give
+// the correctly rounded quotient wherever FAST is chosen (see quant_h).
+template <int R16, bool FAST>
+__device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slot, const float* lamv, int lane,
+                                           int64_t mrow0, int k0, int tn, const uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+  const int r = lane & 15, c = lane >> 4;
+  const int K2 = g.N;
+  uint8_t* const codes = g.nact + g.n_codes;
+  uint8_t* const scales = g.nact + g.n_scales;
+  float* const part = reinterpret_cast<float*>(g.nact + g.n_part);
+  const float* const slam = lamv;
+  const float* const srl = lamv + 256;
+  const float* const srlo = lamv + 512;
+
+  for (int t = 0; t < 4; ++t) {                     // the wave's four 16-row tiles
+    const int row = t * 16 + r;                      // row within the slot
+    const int64_t m = mrow0 + row;
+    v4f dacc[R16 > 0 ? R16 : 1];
 #pragma unroll
-      for (int i = 0; i < WN; ++i)
+    for (int cb = 0; cb < R16; ++cb) dacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[i][e] = div_refined(h[i][e], nlam[16 * i + 4 * q + e], rv[i][e]);
-    } else {
+    for (int s = 0; s < 4; ++s) {                    // 64 columns per step
+      float ah[2][8], x[16];
+      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off(row, s * 64 + c * 8)), ah[0]);
+      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off(row, s * 64 + 32 + c * 8)), ah[1]);
 #pragma unroll
-      for (int i = 0; i < WN; ++i)
+      for (int e = 0; e < 16; ++e) {
+        const int kl = s * 64 + (e >> 3) * 32 + c * 8 + (e & 7);
+        const float a = ah[e >> 3][e & 7];
+        x[e] = FAST ? fmaf(a, srl[kl], a * srlo[kl]) : a / slam[kl];
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[i][e] = h[i][e] / nlam[16 * i + 4 * q + e];
-    }
-    // per block: group maximum over the row's 4 lanes, E8M0 scale, E2M1 codes
-    const int64_t mrow = m0 + 16 * j + r;
+      for (int h = 0; h < 2; ++h) {
+        const int kb = (k0 + s * 64 + h * 32) / 32;  // block index in the next layer's K
+        float amax = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float amax = 0.f;
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+        amax = rowgroup_max(amax);
+        const uint32_t sb = e8m0_of_amax(amax);
+        const float inv = inv_scale_of_e8m0(sb);
+        uint32_t cw = 0;
+        cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
+        cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
+        cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
+        cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+        // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
+        *reinterpret_cast<uint32_t*>(codes + code_chunk(m / 16, kb / 4, K2, (kb & 3) * 16 + r) + c * 4) = cw;
+        if (c == (kb & 3)) scales[mx_scale_byte(m, kb, K2)] = uint8_t(sb);
+        if (R16 > 0) {
+          // down projection: x_hat as a bf16 hi + lo pair against the stored L1' fragments
+          uint4 hi, lo;
+          hi.x = cvt_bf2(x[8 * h + 0], x[8 * h + 1]);
+          hi.y = cvt_bf2(x[8 * h + 2], x[8 * h + 3]);
+          hi.z = cvt_bf2(x[8 * h + 4], x[8 * h + 5]);
+          hi.w = cvt_bf2(x[8 * h + 6], x[8 * h + 7]);
+          lo.x = cvt_bf2(x[8 * h + 0] - bf_lo(hi.x), x[8 * h + 1] - bf_hi(hi.x));
+          lo.y = cvt_bf2(x[8 * h + 2] - bf_lo(hi.y), x[8 * h + 3] - bf_hi(hi.y));
+          lo.z = cvt_bf2(x[8 * h + 4] - bf_lo(hi.z), x[8 * h + 5] - bf_hi(hi.z));
+          lo.w = cvt_bf2(x[8 * h + 6] - bf_lo(hi.w), x[8 * h + 7] - bf_hi(hi.w));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(x[2 * b][e]), fabsf(x[2 * b + 1][e])));
-      amax = rowgroup_max(amax);
-      const uint32_t sb = e8m0_of_amax(amax);
-      const float inv = inv_scale_of_e8m0(sb);
-      uint32_t cw = 0;
-      cw = cvt_fp4x2<0>(cw, x[2 * b][0] * inv, x[2 * b][1] * inv);
-      cw = cvt_fp4x2<1>(cw, x[2 * b][2] * inv, x[2 * b][3] * inv);
-      cw = cvt_fp4x2<2>(cw, x[2 * b + 1][0] * inv, x[2 * b + 1][1] * inv);
-      cw = cvt_fp4x2<3>(cw, x[2 * b + 1][2] * inv, x[2 * b + 1][3] * inv);
-      // lane chunk r + 16 b of the 16-row tile: elements 4q .. 4q+3 in bytes 2q, 2q+1,
-      // elements 16 + 4q .. in bytes 8 + 2q, 9 + 2q
-      uint8_t* chunk = stage + (r + 16 * b) * 16;
-      *reinterpret_cast<uint16_t*>(chunk + 2 * q) = uint16_t(cw);
-      *reinterpret_cast<uint16_t*>(chunk + 8 + 2 * q) = uint16_t(cw >> 16);
-      if (q == b) scales[mx_scale_byte(mrow, ks * 4 + b, K2)] = uint8_t(sb);
-    }
-    *reinterpret_cast<uint4*>(codes + code_chunk((m0 + 16 * j) / 16, ks, K2, lane)) =
-        *reinterpret_cast<const uint4*>(stage + lane * 16);
-    // down projection of the wave's 128 K: x_hat as bf16 hi + lo against L1'
-    if (R16 > 0) {
-      v4f d[kMaxR16];
-#pragma unroll
-      for (int c = 0; c < kMaxR16; ++c) d[c] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        uint4 hi, lo;
-        hi.x = cvt_bf2(x[2 * b][0], x[2 * b][1]);
-        hi.y = cvt_bf2(x[2 * b][2], x[2 * b][3]);
-        hi.z = cvt_bf2(x[2 * b + 1][0], x[2 * b + 1][1]);
-        hi.w = cvt_bf2(x[2 * b + 1][2], x[2 * b + 1][3]);
-        lo.x = cvt_bf2(x[2 * b][0] - bf_lo(hi.x), x[2 * b][1] - bf_hi(hi.x));
-        lo.y = cvt_bf2(x[2 * b][2] - bf_lo(hi.y), x[2 * b][3] - bf_hi(hi.y));
-        lo.z = cvt_bf2(x[2 * b + 1][0] - bf_lo(hi.z), x[2 * b + 1][1] - bf_hi(hi.z));
-        lo.w = cvt_bf2(x[2 * b + 1][2] - bf_lo(hi.w), x[2 * b + 1][3] - bf_hi(hi.w));
-#pragma unroll
-        for (int c = 0; c < kMaxR16; ++c)
-          if (c < R16) {
-            d[c] = mfma_bf16(hi, l1g[b][c], d[c]);
-            d[c] = mfma_bf16(lo, l1g[b][c], d[c]);
+          for (int cb = 0; cb < R16; ++cb) {
+            dacc[cb] = mfma_bf16(hi, l1r[2 * s + h][cb], dacc[cb]);
+            dacc[cb] = mfma_bf16(lo, l1r[2 * s + h][cb], dacc[cb]);
           }
-      }
-      // the two waves of a row range (wn = 0, 1) add their halves in LDS, in that
-      // order; wave wn = 0 writes the workgroup's partial of N tile tn
-      v4f* dr = dred + ((wm * 2 + (j & 1)) * kMaxR16) * 64 + lane;
-      if (wn == 1) {
-#pragma unroll
-        for (int c = 0; c < kMaxR16; ++c)
-          if (c < R16) dr[c * 64] = d[c];
-      }
-      __syncthreads();
-      if (wn == 0) {
-#pragma unroll
-        for (int c = 0; c < kMaxR16; ++c)
-          if (c < R16) {
-            const v4f o = dr[c * 64];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int64_t mm = m0 + 16 * j + (lane >> 4) * 4 + e;
-              part[(size_t(tn) * g.M_pad + mm) * g.nr_pad + c * 16 + r] = d[c][e] + o[e];
-            }
-          }
+        }
       }
     }
-  };
-  static_assert(WM == 8, "eight 16-row tiles per wave");
-  row_tile(std::integral_constant<int, 0>{});
-  row_tile(std::integral_constant<int, 1>{});
-  row_tile(std::integral_constant<int, 2>{});
-  row_tile(std::integral_constant<int, 3>{});
-  row_tile(std::integral_constant<int, 4>{});
-  row_tile(std::integral_constant<int, 5>{});
-  row_tile(std::integral_constant<int, 6>{});
-  row_tile(std::integral_constant<int, 7>{});
+    // lane holds rows (lane / 16) * 4 + e, rank column cb * 16 + lane % 16 of the tile
+#pragma unroll
+    for (int cb = 0; cb < R16; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t mm = mrow0 + t * 16 + (lane >> 4) * 4 + e;
+        part[(size_t(tn) * g.M_pad + mm) * g.nr_pad + cb * 16 + r] = dacc[cb][e];
+      }
+  }
+}
+
+// Phase 2 for wave w.  The smoothing quotients must be the IEEE ones.  The
+// two-operation form gives them when every lambda is in [2^-32, 2^32] and passed
+// the packing-time check, and every value of H is +0 or in [2^-40, 2^60) in
+// magnitude (the activation kernel's conditions); a first pass over the wave's
+// rows checks the values, and a wave with any value outside takes IEEE division
+// for all of its rows (same quotients, slower).
+template <int R16>
+__device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, const float* lamv, int lane,
+                                        int64_t mrow0, int k0, int tn, const uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+  const int r = lane & 15, c = lane >> 4;
+  const uint32_t wf = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(g.nblob + g.n_flags));
+  bool oor = false;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      oor = oor || exp_out_of_range(*reinterpret_cast<const uint4*>(slot + htile_off(t * 16 + r, s * 64 + c * 8)),
+                                    *reinterpret_cast<const uint4*>(slot + htile_off(t * 16 + r, s * 64 + 32 + c * 8)));
+  const bool fast = (wf & (kLamRangeBit | kDivSlowBit)) == 0 && !__any(oor);
+  if (__builtin_expect(fast, 1))
+    quant_rows<R16, true>(g, slot, lamv, lane, mrow0, k0, tn, l1r);
+  else
+    quant_rows<R16, false>(g, slot, lamv, lane, mrow0, k0, tn, l1r);
 }
 
 // Whole epilogue after the main loop: low-rank MFMAs first (their operand loads
@@ -392,7 +373,7 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WN, int WM, bool OUT_F32, bool GELU, bool QOUT = false>
+template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1>
 __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   __shared__ uint4 ring0[kStageU4], ring1[kStageU4], ring2[kStageU4], ring3[kStageU4];   // 4 x 32 KiB
   static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
@@ -518,12 +499,26 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
 #undef SVDQ_FP4_STEP
   // every wave passed the last barrier with no load in flight: the ring is free
   // for the output staging (one slot per wave)
-  if constexpr (QOUT) {
+  if constexpr (QOUT >= 0) {                        // QOUT = the next layer's rank tiles of 16
+    // lambda, 1/lambda and the correction of the next layer for this tile's 256 columns
+    __shared__ float lamv[3 * 256];
+    {
+      const int k = int(threadIdx.x);
+      const int64_t kn = nt0 * 16 + k;
+      lamv[k] = reinterpret_cast<const float*>(g.nblob + g.n_lam)[kn];
+      lamv[256 + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlam)[kn];
+      lamv[512 + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlo)[kn];
+    }
     add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
-    store_quant<WN, WM, GELU>(g, acc, bv, n0, m0, lane, wn, wm, tn, reinterpret_cast<uint8_t*>(ring0) + w * 1024,
-                              reinterpret_cast<v4f*>(ring1));
+    uint4 l1r[8][QOUT > 0 ? QOUT : 1];
+    load_l1_next<QOUT>(g, int(nt0 * 16), lane, l1r);
+    stage_h<WN, WM, GELU>(acc, bv, lane, wn, wm, reinterpret_cast<uint8_t*>(ring0), reinterpret_cast<uint8_t*>(ring1),
+                          reinterpret_cast<uint8_t*>(ring2), reinterpret_cast<uint8_t*>(ring3));
+    __syncthreads();
+    quant_h<QOUT>(g, reinterpret_cast<const uint8_t*>(slot(w)), lamv, lane, mt0 * 16 + w * 64, int(nt0 * 16), tn,
+                  l1r);
   } else {
     epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
@@ -659,10 +654,17 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
   g.n_codes = nal.codes; g.n_scales = nal.scales; g.n_part = nal.part;
   g.nr_pad = int(nwl.r_pad);
   const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-  if (epi & SVDQ_EPI_GELU)
-    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, true>), dim3(nb), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, true>), dim3(nb), dim3(256), 0, s, g);
+  const bool gelu = (epi & SVDQ_EPI_GELU) != 0;
+#define SVDQ_QLAUNCH(R16)                                                                                    \
+  if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
+  else hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, R16>), dim3(nb), dim3(256), 0, s, g)
+  switch (nwl.r_pad / 16) {
+    case 0: SVDQ_QLAUNCH(0); break;
+    case 2: SVDQ_QLAUNCH(2); break;
+    case 4: SVDQ_QLAUNCH(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SVDQ_QLAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nwl.r_pad == 0) return e;
   return launch_reduce_down(reinterpret_cast<const float*>(nact + nal.part), N / kTileRows, nal.M_pad,

@@ -117,10 +117,6 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
 // reciprocal division (same result as IEEE division, far fewer operations); the
 // group maximum over the 4 lanes of a row uses the VALU lane swaps.
 
-__device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
-  a[0] = bf_lo(r.x); a[1] = bf_hi(r.x); a[2] = bf_lo(r.y); a[3] = bf_hi(r.y);
-  a[4] = bf_lo(r.z); a[5] = bf_hi(r.z); a[6] = bf_lo(r.w); a[7] = bf_hi(r.w);
-}
 
 constexpr int kActStep = 64;   // K per pipeline step: two 32-blocks (one INT4 group)
 constexpr int kActDepth = 3;   // steps of X in flight ahead of the one being computed
@@ -204,7 +200,7 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
     // scale) equal the IEEE quotient when |x| is in [2^-40, 2^60) and lambda in
     // [2^-32, 2^32]: every product, quotient and remainder then stays far inside
     // the normal range.  Checked on the bf16 exponent fields, two per dword: the
-    // biased exponent must lie in [87, 187).  Zeros and subnormals fail too.
+    // biased exponent must lie in [87, 187) (+0 passes; -0 and subnormals fail).
     const bool fast = !ieee_only && !__any(exp_out_of_range(xa, xb));
     float x[16];
 #pragma unroll
