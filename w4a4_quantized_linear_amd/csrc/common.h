@@ -23,14 +23,14 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
-
-// Two fp32 -> packed bf16 pair, round to nearest even, with the gfx950 convert.
+// Two fp32 -> packed bf16 pair, round to nearest even, with the gfx950 convert
+// (one instruction; a in the low half).
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return cvt_bf2(a, b); }
 
 // a / b correctly rounded, given r = 1/b correctly rounded: the estimate a r is
 // refined twice with fused multiply-adds (q <- q + (a - q b) r); the first step
