@@ -538,8 +538,25 @@ __device__ __forceinline__ void unpack_frag(const uint4& q, v4i& g0, v4i& g1) {
   g1 = v4i{e0, o0, e1, o1};
 }
 
+// 256 threads = 4 waves in 2 x 2; workgroup tile 2 WN x 2 WM blocks of 16 x 16,
+// wave tile WN x WM.  Per 128-K step a wave needs its WN weight and WM activation
+// fragments (one coalesced 1 KiB load each) and their fp16 scales; these are
+// loaded one step ahead into a second register set, so their latency hides
+// behind the current step.  The nibbles are unpacked to int8,
+// v_mfma_i32_16x16x64_i8 gives each 64-group's exact int32 sum, and sW sX times
+// that sum is added to the fp32 accumulators.  That rescale (int -> float, the
+// scale product, a fused multiply-add per output and group) is VALU work no
+// matrix instruction takes over, so this kernel is bound by the VALU rather than
+// the MFMA rate: 3 M N K / 64 lane operations.
+template <int WN, int WM>
+struct Int4Stage {
+  uint4 cw[WN], cx[WM];   // raw codes: weight and activation fragments
+  uint4 sw[WN];           // weight scales: the lane's 4 rows x 2 groups (fp16)
+  uint32_t sx[WM];        // activation scales: the lane's row x 2 groups (fp16)
+};
+
 template <int WN, int WM, bool OUT_F32, bool GELU>
-__global__ void __launch_bounds__(256) gemm_int4_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
@@ -557,45 +574,70 @@ __global__ void __launch_bounds__(256) gemm_int4_kernel(GemmArgs g) {
   const int64_t wrow = n0 + (lane >> 4) * 4;  // first of the lane's 4 weight rows in block 0
   const int64_t arow = m0 + (lane & 15);
 
+  auto load = [&](int ks, Int4Stage<WN, WM>& st) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      st.cw[i] = Wc[(size_t(i) * KS + ks) * 64];
+      st.sw[i] = Wsc[(size_t(ks) * g.N_pad + wrow + i * 16) / 4];  // 4 rows x 2 fp16 per 16 B
+    }
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      st.cx[j] = Ac[(size_t(j) * KS + ks) * 64];
+      st.sx[j] = Asc[size_t(ks) * g.M_pad + arow + j * 16];
+    }
+  };
+
   v4f acc[WN][WM];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < KS; ++ks) {
-    v4i A0[WN], A1[WN], B0[WM], B1[WM];
-    float sw0[WN][4], sw1[WN][4], sx0[WM], sx1[WM];
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      unpack_frag(Wc[(size_t(i) * KS + ks) * 64], A0[i], A1[i]);
-      const uint4 s = Wsc[(size_t(ks) * g.N_pad + wrow + i * 16) / 4];  // 4 rows x 2 fp16 per 16 B
-      sw0[i][0] = h2f(s.x); sw1[i][0] = h2f(s.x >> 16);
-      sw0[i][1] = h2f(s.y); sw1[i][1] = h2f(s.y >> 16);
-      sw0[i][2] = h2f(s.z); sw1[i][2] = h2f(s.z >> 16);
-      sw0[i][3] = h2f(s.w); sw1[i][3] = h2f(s.w >> 16);
-    }
+  auto compute = [&](const Int4Stage<WN, WM>& st) {
+    v4i b0[WM], b1[WM];
+    float sx0[WM], sx1[WM];
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
-      unpack_frag(Ac[(size_t(j) * KS + ks) * 64], B0[j], B1[j]);
-      const uint32_t s = Asc[size_t(ks) * g.M_pad + arow + j * 16];
-      sx0[j] = h2f(s);
-      sx1[j] = h2f(s >> 16);
+      unpack_frag(st.cx[j], b0[j], b1[j]);
+      sx0[j] = h2f(st.sx[j]);
+      sx1[j] = h2f(st.sx[j] >> 16);
     }
 #pragma unroll
-    for (int i = 0; i < WN; ++i)
+    for (int i = 0; i < WN; ++i) {
+      v4i a0, a1;
+      unpack_frag(st.cw[i], a0, a1);
+      const uint32_t swv[4] = {st.sw[i].x, st.sw[i].y, st.sw[i].z, st.sw[i].w};
+      float sw0[4], sw1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sw0[e] = h2f(swv[e]);
+        sw1[e] = h2f(swv[e] >> 16);
+      }
 #pragma unroll
       for (int j = 0; j < WM; ++j) {
-        const v4i p0 = mfma_i8(A0[i], B0[j]);
-        const v4i p1 = mfma_i8(A1[i], B1[j]);
+        const v4i p0 = mfma_i8(a0, b0[j]);
+        const v4i p1 = mfma_i8(a1, b1[j]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[i][j][e] = fmaf(float(p0[e]), sw0[i][e] * sx0[j], acc[i][j][e]);
-          acc[i][j][e] = fmaf(float(p1[e]), sw1[i][e] * sx1[j], acc[i][j][e]);
+          acc[i][j][e] = fmaf(float(p0[e]), sw0[e] * sx0[j], acc[i][j][e]);
+          acc[i][j][e] = fmaf(float(p1[e]), sw1[e] * sx1[j], acc[i][j][e]);
         }
       }
+    }
+  };
+
+  // KS is a multiple of 4 (K % 512 == 0): two steps per iteration, each
+  // computing one register set while the other fills; the final load repeats
+  // the last step (in bounds, unused).
+  Int4Stage<WN, WM> s0, s1;
+  load(0, s0);
+  for (int ks = 0; ks < KS; ks += 2) {
+    load(ks + 1, s1);
+    compute(s0);
+    load(ks + 2 < KS ? ks + 2 : KS - 1, s0);
+    compute(s1);
   }
-  __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];
+  __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
   epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
 }
 
