@@ -347,8 +347,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 // superfragment (one dword per lane and 16-row tile) are loaded one
 // superfragment ahead; the MFMA of step u of the superfragment picks byte u.
 
-constexpr int kStageFrags = 16;                 // fragments per operand per stage
-constexpr int kStageU4 = 2 * kStageFrags * 64;  // uint4 per stage (weights, then activations)
 
 __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -374,13 +372,18 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1>
-__global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
-  __shared__ uint4 ring0[kStageU4], ring1[kStageU4], ring2[kStageU4], ring3[kStageU4];   // 4 x 32 KiB
-  static_assert(WN == 8 && WM == 8, "tile shape is fixed by the staging scheme");
+__global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
+  static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
+  static_assert(QOUT < 0 || WN == 8, "the fused quantization takes 256 x 256 tiles");
+  constexpr int SF = 2 * WN;            // fragments per operand per stage
+  constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
+  constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
+  static_assert(2 * PW == WN, "each wave row issues one fragment load per step");
+  __shared__ uint4 ring0[SU4], ring1[SU4], ring2[SU4], ring3[SU4];   // 4 x 32 KiB (8 x 8) or 4 x 16 KiB
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = w & 1, wm = w >> 1;               // 2 x 2 waves
-  constexpr int BN = 256, BM = 256;
+  constexpr int BN = 32 * WN, BM = 32 * WM;
   const int tiles_m = int(g.M_pad / BM);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = t % tiles_m, tn = t / tiles_m;
@@ -391,8 +394,8 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   const int64_t m0 = (mt0 + wm * WM) * 16;
   auto slot = [&](int u) -> uint4* { return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3; };
 
-  // Per-workgroup views of the operands: 16 row tiles of codes and of scales each.
-  const uint32_t code_bytes = uint32_t(kStageFrags) * KS * 1024, scale_bytes = uint32_t(kStageFrags) * KSUP * 256;
+  // Per-workgroup views of the operands: SF row tiles of codes and of scales each.
+  const uint32_t code_bytes = uint32_t(SF) * KS * 1024, scale_bytes = uint32_t(SF) * KSUP * 256;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.wblob + g.w_codes + size_t(nt0) * KS * 1024, code_bytes);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.act + g.a_codes + size_t(mt0) * KS * 1024, code_bytes);
   const __amdgpu_buffer_rsrc_t rSA = make_rsrc(g.wblob + g.w_scales + size_t(nt0) * KSUP * 256, scale_bytes);
@@ -409,14 +412,16 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
     for (int j = 0; j < WM; ++j)
       y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WM + j) * KSUP + sup) * 256, 0);
   };
-  // This wave's share of a stage: weight fragments 4w .. 4w+3 (f = 0..3) and
-  // activation fragments 4w .. 4w+3 (f = 4..7).
+  // This wave's share of a stage: weight fragments PW w .. PW w + PW-1 (f < PW)
+  // and the activation fragments of the same numbers (PW <= f < 2 PW).
   auto fetch1 = [&](uint4* dst_stage, int step, int f) {
-    const uint32_t so = uint32_t((4 * w + (f & 3)) * KS + step) * 1024;
-    load_frag_lds(f < 4 ? rA : rB, dst_stage + ((f < 4 ? 0 : kStageFrags) + 4 * w + (f & 3)) * 64, voff16, so);
+    const bool wt = f < PW;
+    const int fi = wt ? f : f - PW;
+    const uint32_t so = uint32_t((PW * w + fi) * KS + step) * 1024;
+    load_frag_lds(wt ? rA : rB, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
   };
   auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
-  auto frag_b = [&](const uint4* st, int j) { return st[(kStageFrags + wm * WM + j) * 64 + lane]; };
+  auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WM + j) * 64 + lane]; };
 
   // Prologue: scales of superfragment 0, then stages 0..2 into slots 0..2.
   v4f acc[WN][WM];
@@ -426,12 +431,12 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
     for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   load_scales(sa, sb, 0);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(ring0, 0, f);
+  for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(ring1, 1, f);
+  for (int f = 0; f < 2 * PW; ++f) fetch1(ring1, 1, f);
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fetch1(ring2, 2, f);
-  wait_barrier<8>();                               // stages 0 and 1 are in LDS
+  for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+  wait_barrier<2 * PW>();                          // stages 0 and 1 are in LDS
   // Fragments in registers, reloaded in place.  A step runs its 8 x 8 MFMAs in
   // two halves by activation fragment: half 0 uses fb[0..3] and meanwhile reads
   // fb[4..7] of the same stage; half 1 uses fb[4..7] and meanwhile reads the
@@ -444,7 +449,7 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   for (int i = 0; i < WN; ++i) fa[i] = frag_a(ring0, i);
 
   // Step U of a superfragment.  Row i also issues one fragment load of stage
-  // step+3.  The flags drop the loads / reads of stages past the end in the
+  // step+3 (2 PW = WN loads per step).  The flags drop the loads / reads of stages past the end in the
   // peeled last superfragment (peeling keeps the loop body free of branches);
   // VM is the number of vector-memory operations the step itself issues.  The
   // scheduling barriers keep each row's memory operations between its MFMAs
@@ -480,10 +485,10 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   int sup = 0;
   for (; sup + 1 < KSUP; ++sup) {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, false, 8)
-    SVDQ_FP4_STEP(1, true, true, true, 8 + WN + WM)
-    SVDQ_FP4_STEP(2, true, true, false, 8)
-    SVDQ_FP4_STEP(3, true, true, false, 8)
+    SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
+    SVDQ_FP4_STEP(1, true, true, true, 2 * PW + WN + WM)
+    SVDQ_FP4_STEP(2, true, true, false, 2 * PW)
+    SVDQ_FP4_STEP(3, true, true, false, 2 * PW)
 #pragma unroll
     for (int i = 0; i < WN; ++i) sa[i] = san[i];
 #pragma unroll
@@ -491,7 +496,7 @@ __global__ void __launch_bounds__(256) gemm_mxfp4_kernel(GemmArgs g) {
   }
   {
     const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, false, 8)
+    SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
     SVDQ_FP4_STEP(1, false, true, false, 0)
     SVDQ_FP4_STEP(2, false, true, false, 0)
     SVDQ_FP4_STEP(3, false, false, false, 0)
@@ -643,6 +648,8 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ launcher
 
+constexpr unsigned kMinBigTiles = 128;   // MXFP4: fewer 256 x 256 tiles than this -> 128 x 128 tiles
+
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
   GemmArgs g;
@@ -664,8 +671,14 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     else hipLaunchKernelGGL((KERNEL<WN, WM, false, false>), dim3(NB), dim3(THREADS), 0, s, g);              \
   } while (0)
   if (fmt == kFmtMXFP4) {
-    const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-    SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, nb);
+    // 256 x 256 tiles when they fill the chip, else 128 x 128 tiles (up to two
+    // workgroups per CU, so one's epilogue overlaps the other's main loop)
+    const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+    if (big >= kMinBigTiles) {
+      SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
+    } else {
+      SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
+    }
   } else {
     const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
     SVDQ_LAUNCH(gemm_int4_kernel, 4, 4, 256, nb);
