@@ -111,6 +111,25 @@ def test_layer_elementwise(torch_dev, case):
     check_fp32_output(Yg.cpu().numpy(), Ly.gelu(Y_o), "GELU output")
 
 
+def test_tile_schedules_elementwise(torch_dev):
+    """The MXFP4 GEMM picks its tiles by the size of the output: 256 x 256 tiles,
+    a partial last round of them split into 128 x 128 quarters in a second
+    launch, or 128 x 128 tiles throughout.  Each schedule, element by element
+    against the oracle: 2048 x 8448 (264 big tiles: 256 + 8 split into 32
+    quarters), 1024 x 512 (8 big tiles: quarters only)."""
+    torch, dev = torch_dev
+    for (M, N, seed) in [(2048, 8448, 41), (1024, 512, 42)]:
+        K = 512
+        spec, L = _medium_layer("qkv", "mxfp4", M, K, N, 16, seed)
+        layer = sq.Layer("mxfp4", K, N, 16)
+        print(f"tile schedule M={M} N={N}", flush=True)
+        w = pack(layer, L, torch, dev)
+        Y = sq.linear(layer, w, dev_tensor(L["X"], torch, dev), sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+        torch.cuda.synchronize()
+        ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")
+        check_fp32_output(Y.cpu().numpy(), ref["Y"], f"M={M} N={N}")
+
+
 def test_gelu_epilogue_pointwise(torch_dev):
     """The GEMM's GELU against the exact erf form, value by value: with R = 0,
     rank 0 and lambda = 1 the output is GELU(b), so the bias carries the test

@@ -34,6 +34,10 @@ struct GemmArgs {
   int K, N, r_pad;
   uint32_t epi;
   void* Y;
+  // MXFP4 with 128 x 128 tiles: -1 covers the whole output; t >= 0 covers the
+  // quarters of the 256 x 256 tiles t, t + 1, ... (in the tile order of the
+  // 256 x 256 launch, which took the tiles before t).
+  int tile0;
   // Output quantized for the next layer instead of Y (its K is N): that layer's
   // packed weights (lambda, 1/lambda, the correction, L1, flags) and activation
   // workspace (codes, scales, down-projection partials).
@@ -385,8 +389,18 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   const int wn = w & 1, wm = w >> 1;               // 2 x 2 waves
   constexpr int BN = 32 * WN, BM = 32 * WM;
   const int tiles_m = int(g.M_pad / BM);
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = t % tiles_m, tn = t / tiles_m;
+  int tm, tn;
+  {
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
+    if (g.tile0 < 0) {
+      tm = t % tiles_m;
+      tn = t / tiles_m;
+    } else {                                       // quarter t % 4 of 256 x 256 tile tile0 + t / 4
+      const int tb = g.tile0 + t / 4, q = t % 4, tmb = int(g.M_pad / 256);
+      tm = (tb % tmb) * 2 + (q & 1);
+      tn = (tb / tmb) * 2 + (q >> 1);
+    }
+  }
   const int64_t nt0 = int64_t(tn) * (BN / 16);    // first 16-row weight tile of the workgroup
   const int64_t mt0 = int64_t(tm) * (BM / 16);
   const int KS = g.K / kKStep, KSUP = g.K / kKSuper;
@@ -652,7 +666,7 @@ constexpr unsigned kMinBigTiles = 128;   // MXFP4: fewer 256 x 256 tiles than th
 
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
-  GemmArgs g;
+  GemmArgs g{};
   g.wblob = wblob;
   g.act = act;
   g.w_codes = wl.codes; g.w_scales = wl.scales; g.w_L2 = wl.L2; g.w_bias = wl.bias;
@@ -672,10 +686,26 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
   } while (0)
   if (fmt == kFmtMXFP4) {
     // 256 x 256 tiles when they fill the chip, else 128 x 128 tiles (up to two
-    // workgroups per CU, so one's epilogue overlaps the other's main loop)
+    // workgroups per CU).  A last partial round of 256 x 256 tiles that fits in
+    // one round of 128 x 128 quarters (two per CU) runs as quarters, in a second
+    // launch: half a big round instead of a whole one.
     const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+    g.tile0 = -1;
     if (big >= kMinBigTiles) {
-      SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      const unsigned rem = big % unsigned(cus), full = big - rem;
+      if (full > 0 && rem > 0 && rem * 4 <= 2 * unsigned(cus)) {
+        SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, full);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g.tile0 = int(full);
+        SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, rem * 4);
+      } else {
+        SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
+      }
     } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
     }
@@ -703,6 +733,7 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
   g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
   g.epi = epi;
   g.Y = nullptr;
+  g.tile0 = -1;
   g.nblob = nblob;
   g.nact = nact;
   g.n_lam = nwl.lam; g.n_rlam = nwl.rlam; g.n_rlo = nwl.rlo; g.n_L1 = nwl.L1; g.n_flags = nwl.flags;
