@@ -173,8 +173,44 @@ def gpu_leg(args):
     fused = None
     if args.workload == "mlp_mxfp4":
         fused = fused_pair(args, sq, torch, layers, weights, inputs[0], ws, outs, epis, M, sum(flops))
+    elif args.workload == "qkv":
+        fused = fused_qkv(args, sq, synth, torch, np, layers[0], weights[0], inputs[0], ws[0], outs[0], epis[0], M,
+                          flops[0])
     return dict(value=value, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps, roofline=roofline,
                 breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused)
+
+
+def fused_qkv(args, sq, synth, torch, np, layer, w, x, ws, out, epi, M, flops):
+    """The QKV layer with the Q/K RMS normalization and rotary embedding in the
+    GEMM epilogue (svdq_gemm_qkv), same inputs and step count."""
+    E = synth.draw_qkv_extras(M)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    wq, wk, cs, sn = t(E["norm_q"]), t(E["norm_k"]), t(E["cos"]), t(E["sin"])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sq.quantize_act(layer, w, x, out=ws)
+        if ev is not None:
+            ev[1].record()
+        sq.gemm_qkv(layer, w, ws, M, epi, wq, wk, E["eps"], cs, sn, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    seg = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) * 1e3 / args.steps
+           for i in range(2)]
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
+            "quantize_us": round(seg[0], 2), "gemm_qkv_us": round(seg[1], 2),
+            "launches": "quantize_act; gemm_qkv (GEMM with Q/K RMS norm and rotary embedding in the epilogue)"}
 
 
 def fused_pair(args, sq, torch, layers, weights, x, ws, outs, epis, M, flops):
@@ -266,7 +302,7 @@ def main():
         "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4),
     }
     if r["fused"] is not None:
-        line["fused_mlp"] = r["fused"]
+        line["fused_mlp" if args.workload == "mlp_mxfp4" else "fused_qkv"] = r["fused"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(specs)
     print(json.dumps(line), flush=True)

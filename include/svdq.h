@@ -146,6 +146,26 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
                             uint32_t epi, const svdq_layer_desc* dn, const void* wn_packed, void* an_packed,
                             void* stream);
 
+/* Fused QKV step: launch 2 of a layer whose N = 3 H head_dim outputs are [Q | K | V]
+ * (the Nunchaku in Diffusers page, section "Quantizing your own model": the FLUX.1
+ * to_qkv projection feeds one operator that also applies the Q/K normalization
+ * modules and the rotary embedding).  With y = acc + (X_hat L1) L2 + b in fp32
+ * (epi: SVDQ_EPI_LOWRANK and / or SVDQ_EPI_BIAS only), for every token m and every
+ * Q head (weight norm_q) and K head (weight norm_k):
+ *     z = y / sqrt(mean over the head's features of y^2 + eps) * w,
+ *     (z[2p], z[2p+1]) -> (z[2p] c - z[2p+1] s, z[2p] s + z[2p+1] c),
+ *     c = rope_cos[m][p], s = rope_sin[m][p];
+ * V heads are y.  Y receives the bf16 (nearest even) result, M x N, row stride ldy.
+ *   head_dim  must be 128; N a multiple of 384; MXFP4 only (else SVDQ_ERR_FORMAT)
+ *   norm_q, norm_k  device, bf16 bits [128], 16-byte aligned
+ *   eps       in [0, 1]
+ *   rope_cos, rope_sin  device, float32, M x 64 row-major (angle of pair p of token m),
+ *             16-byte aligned
+ * Other checks and errors as svdq_gemm. */
+svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M,
+                          uint32_t epi, int32_t head_dim, const uint16_t* norm_q, const uint16_t* norm_k, float eps,
+                          const float* rope_cos, const float* rope_sin, void* Y, int64_t ldy, void* stream);
+
 /* Both launches; workspace >= svdq_act_bytes(d, M) bytes (device, 256-aligned). */
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
                         int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi,

@@ -20,6 +20,9 @@ diffusion inference in Diffusers" page; SVDQuant abstract, arXiv 2411.05007):
                   the smoothed weight, its truncated SVD (section 4.2,
                   W_hat = L1 L2 + R with L1 = U Sigma_r, L2 = V_r^T), the 16-bit
                   factors and the residual R.
+* qkv.py       -- the fused QKV step's Q/K RMS normalization and rotary
+                  embedding on the layer output (the Nunchaku in Diffusers
+                  page, section "Quantizing your own model").
 * layer.py     -- the layer output of section 4.2:
                   X W = X_hat W_hat ~ X_hat L1 L2 + Q(X_hat) Q(R), plus bias and
                   an optional GELU, in float64; the error measure and bound of

@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     draw_activations,
     draw_layer,
+    draw_qkv_extras,
     draw_raw,
     layer_spec,
 )

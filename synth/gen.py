@@ -250,3 +250,25 @@ def draw_layer(spec: LayerSpec, seed: Optional[int] = None, with_lora: bool = Tr
         out["L1"] = np.ascontiguousarray(np.concatenate([L1b, out["A"]], axis=1))
         out["L2"] = np.ascontiguousarray(np.concatenate([L2b, out["B"]], axis=0))
     return out
+
+
+# ---------------------------------------------------------------------------
+# inputs of the fused QKV step
+# ---------------------------------------------------------------------------
+
+
+def draw_qkv_extras(M: int, head_dim: int = 128, seed: int = 2) -> dict:
+    """Inputs of the Q/K normalization and rotary embedding of the fused QKV
+    step: the two normalization weights (bf16[head_dim], around 1) and the
+    rotary cos / sin per token and pair (fp32, M x head_dim/2).  Angles follow
+    the usual rotary recipe, position times a geometric frequency ladder
+    10000^(-2p / head_dim), with token positions a random permutation of 0..M-1
+    (so rows do not share angles)."""
+    rng = np.random.default_rng(seed * 1_000_003 + 4099)
+    wq = bf16_bits_from_f32((1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32))
+    wk = bf16_bits_from_f32((1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32))
+    pos = rng.permutation(M).astype(np.float64)
+    freq = 10000.0 ** (-2.0 * np.arange(head_dim // 2) / head_dim)
+    ang = pos[:, None] * freq[None, :]
+    return {"norm_q": wq, "norm_k": wk, "cos": np.cos(ang).astype(np.float32),
+            "sin": np.sin(ang).astype(np.float32), "eps": 1e-6}

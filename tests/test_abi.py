@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 101
+    assert L.svdq_version() == 102
     for s in range(8):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -132,6 +132,23 @@ def test_gemm_quant_validation(L, forced_device_error):
     assert q(d, P, P, 4, 7, dn, P, P + 16, None) == 4    # workspace not 256-aligned
     assert q(d, P, P, 4, 7, dn, P, P, None) == 6         # valid -> device check
     assert q(d, P, P, 0, 7, dn, P, P, None) == 6
+
+
+def test_gemm_qkv_validation(L, forced_device_error):
+    f = L.svdq_gemm_qkv
+    d = ctypes.byref(D(K=1024, N=768, rank=16))          # [Q | K | V], two heads of 128 each
+    ok = (P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P, 768, None)
+    assert f(d, *ok) == 6                                 # valid -> device check
+    assert f(None, *ok) == 1
+    assert f(d, P, P, 4, 3, 128, None, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 1    # norm_q
+    assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), None, P, P, 768, None) == 1    # rope_cos
+    assert f(d, P, P, 4, 3, 64, P, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 2       # head_dim
+    assert f(ctypes.byref(D(K=1024, N=512)), P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P, 512, None) == 2
+    assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(-1.0), P, P, P, 768, None) == 2       # eps
+    assert f(d, P, P, 4, 7, 128, P, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 3       # GELU flag
+    assert f(ctypes.byref(D(fmt=2, K=1024, N=768)), *ok) == 3                                 # INT4
+    assert f(d, P, P, 4, 3, 128, P + 8, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 4   # norm_q aligned
+    assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P + 8, 768, None) == 4   # Y aligned
 
 
 def test_unpack_validation(L, forced_device_error):

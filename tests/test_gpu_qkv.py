@@ -1,0 +1,83 @@
+"""Fused QKV step (svdq_gemm_qkv): the [Q | K | V] projection with the Q/K RMS
+normalization and the rotary embedding in the GEMM epilogue, against the
+oracle's layer output passed through oracle/qkv.py (float64), element by
+element at a medium size and on sampled tokens (all of their heads) at the
+FLUX QKV size.  The V heads must equal svdq_gemm's bf16 output bit for bit."""
+import numpy as np
+import pytest
+
+import synth
+import w4a4_quantized_linear_amd as sq
+from oracle import layer as Ly
+from oracle import qkv as QK
+from oracle import formats as F
+
+from _gpu_helpers import bf16_to_np, check_bf16_output, dev_tensor, pack
+
+pytestmark = pytest.mark.gpu
+
+EPI = sq.EPI_LOWRANK | sq.EPI_BIAS
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sq.lib()
+    assert sq.device_check(), "current device is not gfx950"
+    return torch, torch.device("cuda:0")
+
+
+def _run(torch, dev, L, E, layer, M):
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    Yq = sq.gemm_qkv(layer, w, ws, M, EPI, dev_tensor(E["norm_q"], torch, dev), dev_tensor(E["norm_k"], torch, dev),
+                     E["eps"], dev_tensor(E["cos"], torch, dev), dev_tensor(E["sin"], torch, dev))
+    Yp = sq.gemm(layer, w, ws, M, EPI)
+    torch.cuda.synchronize()
+    return Yq, Yp
+
+
+def _oracle(Y_o, E):
+    return QK.qkv_norm_rope(Y_o, 128, F.bf16_value(E["norm_q"]), F.bf16_value(E["norm_k"]), E["eps"],
+                            E["cos"], E["sin"])
+
+
+@pytest.mark.parametrize("M,K,N,rank,seed", [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3)])
+def test_qkv_elementwise(torch_dev, M, K, N, rank, seed):
+    torch, dev = torch_dev
+    spec = synth.layer_spec("qkv", M=M, K=K, N=N, rank=rank, x_outliers=max(1, K // 100),
+                            w_outliers=max(1, K // 100), lora_rank=0)
+    L = synth.draw_layer(spec, seed=seed)
+    E = synth.draw_qkv_extras(M, seed=seed)
+    layer = sq.Layer("mxfp4", K, N, rank)
+    print(f"qkv M={M} K={K} N={N} r={rank}", flush=True)
+    Yq, Yp = _run(torch, dev, L, E, layer, M)
+    Y_o = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")["Y"]
+    want = _oracle(Y_o, E)
+    got = bf16_to_np(Yq)
+    hd = N // 3
+    check_bf16_output(got[:, :2 * hd], want[:, :2 * hd], "normalized and rotated Q | K")
+    check_bf16_output(got[:, 2 * hd:], want[:, 2 * hd:], "V")
+    assert torch.equal(Yq[:, 2 * hd:].view(torch.int16), Yp[:, 2 * hd:].view(torch.int16)), "V differs from svdq_gemm"
+
+
+def test_qkv_full_size_sampled_tokens(torch_dev):
+    """FLUX QKV: M=4608, K=3072 -> N=9216 (24 heads each of Q, K, V), rank 32."""
+    torch, dev = torch_dev
+    spec = synth.CONFIGS["qkv"]
+    L = synth.draw_layer(spec)
+    E = synth.draw_qkv_extras(spec.M, seed=7)
+    layer = sq.Layer("mxfp4", spec.K, spec.N, spec.rank)
+    print("qkv full size", flush=True)
+    Yq, Yp = _run(torch, dev, L, E, layer, spec.M)
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, spec.M - 1], rng.choice(spec.M, 30, replace=False)]))
+    Y_o = Ly.forward_rows(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4", rows)
+    Es = dict(E, cos=E["cos"][rows], sin=E["sin"][rows])
+    want = _oracle(Y_o, Es)
+    got = bf16_to_np(Yq)[rows]
+    check_bf16_output(got, want, "FLUX QKV, sampled tokens")
+    hd = spec.N // 3
+    assert torch.equal(Yq[:, 2 * hd:].view(torch.int16), Yp[:, 2 * hd:].view(torch.int16)), "V differs from svdq_gemm"

@@ -118,6 +118,21 @@ def gemm_quant(layer: Layer, w_packed, a_packed, M: int, epi: int, next_layer: L
     return out
 
 
+def gemm_qkv(layer: Layer, w_packed, a_packed, M: int, epi: int, norm_q, norm_k, eps: float, rope_cos, rope_sin,
+             head_dim: int = 128, out=None, stream=None):
+    """Launch 2 of a fused [Q | K | V] layer with the Q/K RMS normalization (weights
+    norm_q, norm_k: bf16[head_dim]) and the rotary embedding (rope_cos, rope_sin:
+    fp32 M x head_dim/2) in the epilogue; returns Y (M x N bf16)."""
+    torch = _torch()
+    d, p = _desc_ref(layer)
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=torch.bfloat16, device=w_packed.device)
+    st = lib().svdq_gemm_qkv(p, _ptr(w_packed), _ptr(a_packed), M, epi, head_dim, _ptr(norm_q), _ptr(norm_k),
+                             float(eps), _ptr(rope_cos), _ptr(rope_sin), _ptr(out), out.stride(0), _stream(stream))
+    check("svdq_gemm_qkv", st)
+    return out
+
+
 def linear(layer: Layer, w_packed, X, epi: int, out=None, workspace=None, stream=None):
     """Both launches: Y = act(deQ(Q(X/lam)) deQ(Q(R))^T + (X/lam L1) L2 + b)."""
     torch = _torch()

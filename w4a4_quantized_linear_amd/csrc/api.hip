@@ -23,6 +23,10 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
 hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                              int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
                              uint8_t* nact, const ActLayout& nal, hipStream_t s);
+hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
+                           int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, const uint16_t* norm_q,
+                           const uint16_t* norm_k, float eps, const float* rope_cos, const float* rope_sin,
+                           hipStream_t s);
 hipError_t launch_unpack_weight(int fmt, int K, int N, int rank, const WeightLayout& wl, const uint8_t* blob,
                                 uint8_t* codes, void* scales, uint16_t* L1, uint16_t* L2, float* lam, uint16_t* bias,
                                 hipStream_t s);
@@ -36,6 +40,7 @@ namespace {
 
 constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int kGemmQuantMaxRank = 64;   // next layer's rank in svdq_gemm_quant (4 rank tiles of 16)
+constexpr int kQkvHeadDim = 128;        // svdq_gemm_qkv: one head per 128 output columns of a wave
 constexpr uint32_t kEpiAll = SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU | SVDQ_EPI_OUT_F32;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -102,7 +107,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 101; }
+int svdq_version(void) { return 102; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -205,6 +210,30 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
   return launched(launch_gemm_quant(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                     al, d->K, d->N, M, epi, static_cast<const uint8_t*>(wn_packed), nwl,
                                     static_cast<uint8_t*>(an_packed), nal, static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M,
+                          uint32_t epi, int32_t head_dim, const uint16_t* norm_q, const uint16_t* norm_k, float eps,
+                          const float* rope_cos, const float* rope_sin, void* Y, int64_t ldy, void* stream) {
+  if (!d || !w_packed || !a_packed || !norm_q || !norm_k || (M > 0 && (!Y || !rope_cos || !rope_sin)))
+    return SVDQ_ERR_NULL;
+  svdq_status s = check_shape(d);
+  if (s != SVDQ_OK) return s;
+  if (M < 0 || M > kMaxRows || ldy < d->N || head_dim != kQkvHeadDim || d->N % (3 * kQkvHeadDim) != 0 ||
+      !(eps >= 0.0f && eps <= 1.0f))
+    return SVDQ_ERR_SHAPE;
+  if ((s = check_fmt(d)) != SVDQ_OK) return s;
+  if (d->fmt != SVDQ_MXFP4 || (epi & ~(SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS)) != 0) return SVDQ_ERR_FORMAT;
+  if (!aligned(w_packed, 256) || !aligned(a_packed, 256) || !aligned(norm_q, 16) || !aligned(norm_k, 16) ||
+      (M > 0 && (!aligned(Y, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))) || ldy % 8 != 0)
+    return SVDQ_ERR_ALIGN;
+  if ((s = device_check()) != SVDQ_OK) return s;
+  if (M == 0) return SVDQ_OK;
+  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->K, d->rank, M);
+  return launched(launch_gemm_qkv(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
+                                  al, d->K, d->N, M, Y, ldy, epi, norm_q, norm_k, eps, rope_cos, rope_sin,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M, int64_t ldx,

@@ -116,6 +116,17 @@ __device__ __forceinline__ float rowgroup_max(float v) {
   return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
+// sum over the lanes l, l ^ 16, l ^ 32, l ^ 48: rows 0+1 and 2+3, then the two
+// pair sums (every lane ends with the same value, in a fixed order)
+__device__ __forceinline__ float rowgroup_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t ua = __float_as_uint(a);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(ua, ua, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // True when some of the 16 bf16 values is outside the fast divisions' range:

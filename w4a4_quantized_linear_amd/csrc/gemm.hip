@@ -38,6 +38,13 @@ struct GemmArgs {
   // quarters of the 256 x 256 tiles t, t + 1, ... (in the tile order of the
   // 256 x 256 launch, which took the tiles before t).
   int tile0;
+  // Fused QKV epilogue: Q/K normalization weights (bf16[128]), eps, and the
+  // rotary cos / sin per token and pair (fp32, M x 64).
+  const uint16_t* norm_q;
+  const uint16_t* norm_k;
+  const float* rope_cos;
+  const float* rope_sin;
+  float eps;
   // Output quantized for the next layer instead of Y (its K is N): that layer's
   // packed weights (lambda, 1/lambda, the correction, L1, flags) and activation
   // workspace (codes, scales, down-projection partials).
@@ -316,6 +323,74 @@ __device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, 
     quant_rows<R16, false>(g, slot, lamv, lane, mrow0, k0, tn, l1r);
 }
 
+// Fused QKV epilogue (the next row after the layer: the Nunchaku in Diffusers
+// page, section "Quantizing your own model", describes the grouped to_qkv
+// projection whose output one fused operator normalizes (norm_q, norm_k) and
+// rotates (rotary embedding)).  The N = 3 H 128 outputs are [Q | K | V] and a
+// wave's 128 columns are one head.  For a Q or K head each row is
+// RMS-normalized over the head, y / sqrt(mean(y^2) + eps) * w, and each pair of
+// consecutive features (2p, 2p + 1) is rotated by the row token's angle for p:
+// (a, b) -> (a cos - b sin, a sin + b cos).  All in fp32 from the accumulators
+// (bias included), one bf16 rounding at the store; V heads are stored as is.
+template <int WN, int WM>
+__device__ __forceinline__ void store_qkv(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
+                                          int64_t n0, int64_t m0, int lane, uint8_t* stage) {
+  static_assert(WN == 8, "a wave's 128 columns are one head");
+  const int q = lane >> 4;
+  const int64_t hd = g.N / 3;
+  const int seg = int(n0 / hd);                 // 0: Q, 1: K, 2: V (uniform for the wave)
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] += bv[i][e];
+  if (seg < 2) {
+    const uint16_t* const wnorm = seg == 0 ? g.norm_q : g.norm_k;
+    float wv[WN][4];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const uint2 u = *reinterpret_cast<const uint2*>(wnorm + 16 * i + 4 * q);
+      wv[i][0] = bf_lo(u.x); wv[i][1] = bf_hi(u.x); wv[i][2] = bf_lo(u.y); wv[i][3] = bf_hi(u.y);
+    }
+    // cos / sin of the lane's row in 16-row tile j: features 16 i + 4 q + e are
+    // pairs p = 8 i + 2 q (e = 0, 1) and p + 1 (e = 2, 3); loaded one tile ahead
+    float2 cb[2][WN], sbuf[2][WN];
+    auto load_rot = [&](int j, float2 (&c)[WN], float2 (&sn)[WN]) {
+      const int64_t m = m0 + 16 * j + (lane & 15);
+      const int64_t mc = m < g.M ? m : g.M - 1;  // rows past M are not stored
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        c[i] = *reinterpret_cast<const float2*>(g.rope_cos + mc * 64 + 8 * i + 2 * q);
+        sn[i] = *reinterpret_cast<const float2*>(g.rope_sin + mc * 64 + 8 * i + 2 * q);
+      }
+    };
+    load_rot(0, cb[0], sbuf[0]);
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      if (j + 1 < WM) load_rot(j + 1, cb[(j + 1) & 1], sbuf[(j + 1) & 1]);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(acc[i][j][e], acc[i][j][e], ss);
+      ss = rowgroup_sum(ss);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + g.eps);
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const float2 c = cb[j & 1][i], sn = sbuf[j & 1][i];
+        const float y0 = acc[i][j][0] * inv * wv[i][0], y1 = acc[i][j][1] * inv * wv[i][1];
+        const float y2 = acc[i][j][2] * inv * wv[i][2], y3 = acc[i][j][3] * inv * wv[i][3];
+        acc[i][j][0] = y0 * c.x - y1 * sn.x;
+        acc[i][j][1] = y0 * sn.x + y1 * c.x;
+        acc[i][j][2] = y2 * c.y - y3 * sn.y;
+        acc[i][j][3] = y2 * sn.y + y3 * c.y;
+      }
+    }
+  }
+  store_out<WN, WM, false, false, false>(g, acc, bv, n0, m0, lane, stage);
+}
+
 // Whole epilogue after the main loop: low-rank MFMAs first (their operand loads
 // come before any store), then every bias value, then bias + activation +
 // conversion + stores with no loads in between (the vector-memory counter also
@@ -375,10 +450,11 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1>
+template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(QOUT < 0 || WN == 8, "the fused quantization takes 256 x 256 tiles");
+  static_assert(!QKV || (WN == 8 && QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue takes 128-column heads");
   constexpr int SF = 2 * WN;            // fragments per operand per stage
   constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
   constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
@@ -538,6 +614,11 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     __syncthreads();
     quant_h<QOUT>(g, reinterpret_cast<const uint8_t*>(slot(w)), lamv, lane, mt0 * 16 + w * 64, int(nt0 * 16), tn,
                   l1r);
+  } else if constexpr (QKV) {
+    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    float bv[WN][4];
+    load_bias<WN>(g, n0, lane, bv);
+    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
     epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
@@ -718,6 +799,28 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
 }
 
 hipError_t launch_reduce_down(const float* part, int splits, int64_t rows_pad, int r_pad, uint16_t* Dout, hipStream_t s);
+
+// The GEMM of a fused QKV layer (MXFP4, head dim 128) with the Q/K
+// normalization and rotary embedding in its epilogue; bf16 output.
+hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
+                           int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, const uint16_t* norm_q,
+                           const uint16_t* norm_k, float eps, const float* rope_cos, const float* rope_sin,
+                           hipStream_t s) {
+  GemmArgs g{};
+  g.wblob = wblob;
+  g.act = act;
+  g.w_codes = wl.codes; g.w_scales = wl.scales; g.w_L2 = wl.L2; g.w_bias = wl.bias;
+  g.a_codes = al.codes; g.a_scales = al.scales; g.a_D = al.D;
+  g.N_pad = wl.N_pad; g.M_pad = al.M_pad; g.M = M; g.ldy = ldy;
+  g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
+  g.epi = epi;
+  g.Y = Y;
+  g.tile0 = -1;
+  g.norm_q = norm_q; g.norm_k = norm_k; g.rope_cos = rope_cos; g.rope_sin = rope_sin; g.eps = eps;
+  const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+  hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(nb), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
 
 // The GEMM of one layer with its bf16 output quantized for the next layer (MXFP4
 // both), then the sum of the down-projection partials into that layer's D.
