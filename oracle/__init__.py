@@ -23,6 +23,8 @@ diffusion inference in Diffusers" page; SVDQuant abstract, arXiv 2411.05007):
 * qkv.py       -- the fused QKV step's Q/K RMS normalization and rotary
                   embedding on the layer output (the Nunchaku in Diffusers
                   page, section "Quantizing your own model").
+* w4a16.py     -- the 4-bit weight x 16-bit activation linear of the second
+                  kernel family (AWQ) on the Nunchaku in Diffusers page.
 * layer.py     -- the layer output of section 4.2:
                   X W = X_hat W_hat ~ X_hat L1 L2 + Q(X_hat) Q(R), plus bias and
                   an optional GELU, in float64; the error measure and bound of

@@ -15,5 +15,6 @@ from .gen import (  # noqa: F401
     draw_layer,
     draw_qkv_extras,
     draw_raw,
+    draw_w4a16,
     layer_spec,
 )

@@ -110,10 +110,16 @@ _add(LayerSpec("lora", M=4608, K=3072, N=12288, rank=32, fmt="mxfp4",
                x_outliers=_pct(0.01, 3072), x_factor=50.0,
                w_outliers=_pct(0.01, 3072), w_kind="t3", w_factor=1.0, lora_rank=16))
 
+# The W4A16 (AWQ-style) modulation projection of a FLUX double block: a batch of
+# conditioning vectors (M = 2 tokens) times a 3072 -> 6 x 3072 weight, INT4 g64
+# weights and bf16 activations; no smoothing and no low-rank branch.
+_add(LayerSpec("mod_w4a16", M=2, K=3072, N=18432, rank=0, fmt="int4",
+               x_outliers=0, x_factor=1.0, w_outliers=_pct(0.01, 3072), w_kind="t3", w_factor=1.0))
+
 # Default seeds: one per workload (the workload's position in the list, 1-based;
 # the two layers of the MLP pair share seed 3 and are told apart by salt).
 SEEDS = {"single": 1, "qkv": 2, "fc1_mxfp4": 3, "fc2_mxfp4": 3, "fc1_int4": 3,
-         "fc2_int4": 3, "lowm": 4, "lora": 5}
+         "fc2_int4": 3, "lowm": 4, "lora": 5, "mod_w4a16": 6}
 _SALT = {"fc2_mxfp4": 7919, "fc2_int4": 7919}
 
 
@@ -255,6 +261,17 @@ def draw_layer(spec: LayerSpec, seed: Optional[int] = None, with_lora: bool = Tr
 # ---------------------------------------------------------------------------
 # inputs of the fused QKV step
 # ---------------------------------------------------------------------------
+
+
+def draw_w4a16(spec: LayerSpec, seed: Optional[int] = None) -> dict:
+    """Operands of a W4A16 layer: X (M x K bf16 bits, N(0,1) with the spec's
+    outlier channels), W (N x K fp32, the weight draw of draw_raw transposed:
+    N(0, 0.02) with heavy-tailed outlier rows) and b (N bf16 bits)."""
+    rng = np.random.default_rng(_seed(spec, seed))
+    X, _ = draw_activations(spec, rng)
+    w, _ = _draw_weight(spec, rng)
+    b = rng.standard_normal(spec.N, dtype=np.float32) * np.float32(0.01)
+    return dict(X=X, W=np.ascontiguousarray(w.T), b=bf16_bits_from_f32(b))
 
 
 def draw_qkv_extras(M: int, head_dim: int = 128, seed: int = 2) -> dict:
