@@ -9,6 +9,10 @@ timing, as at load time).  value = (2 M N K of fc1 + of fc2) per step / time.
 Prints one JSON line.  `roofline` is the fc1 GEMM kernel (the dominant launch),
 timed with HIP events around each of its launches inside the timed region.
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+With --workload mod_w4a16 the step is one W4A16 launch (svdq_gemm_w4a16: bf16
+activations times INT4 weights, the memory-bound modulation projection) and
+`roofline` is HBM-bound: algorithmic bytes (codes, scales, X, Y, bias) per
+launch over its event-timed duration.
 For the MXFP4 pair, `fused_mlp` times the same pair with fc1's GEMM quantizing
 its output for fc2 in its epilogue (svdq_gemm_quant: three launches plus the
 down-projection sum instead of four), same inputs, same step count.
@@ -32,6 +36,8 @@ PAIRS = {
     "mlp_int4": ("fc1_int4", "fc2_int4"),
 }
 SINGLE = ("qkv", "lowm", "lora", "single")
+W4A16 = ("mod_w4a16",)
+HBM_PEAK_GBPS = 8000.0                                      # MI355X HBM3E
 
 
 def parse():
@@ -39,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE))
+    p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE) + list(W4A16))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the timed region, copy MIB mebibytes device to device once (a plain copy of "
@@ -180,6 +186,104 @@ def gpu_leg(args):
                 breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused)
 
 
+def w4a16_bytes(M, K, N):
+    """Algorithmic HBM bytes of one W4A16 launch: INT4 codes and fp16 group
+    scales of W, bf16 X, bf16 Y and bf16 bias, each read or written once."""
+    return N * K // 2 + N * (K // 64) * 2 + M * K * 2 + M * N * 2 + N * 2
+
+
+def gpu_leg_w4a16(args):
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a4_quantized_linear_amd as sq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = synth.CONFIGS[args.workload]
+    d = synth.draw_w4a16(spec)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+    layer = sq.Layer("int4", spec.K, spec.N, 0)
+    w0 = sq.pack_weight(layer, t(d["W"]), None, None, t(np.ones(spec.K, np.float32)), t(d["b"]))
+    # The layer's weights are a few tens of MB, well inside the 256 MB last-level
+    # cache; consecutive launches rotate over copies spanning 1 GiB, so every
+    # launch streams its weights from HBM as a model's successive layers would.
+    copies = max(1, -(-(1 << 30) // w0.numel()))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    x = t(d["X"])
+    out = torch.empty((spec.M, spec.N), dtype=torch.bfloat16, device=dev)
+    del d
+    M = spec.M
+    it = [0]
+
+    def step(ev=None):
+        w = ws[it[0] % copies]
+        it[0] += 1
+        if ev is not None:
+            ev[0].record()
+        sq.gemm_w4a16(layer, w, x, sq.EPI_BIAS, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    launch_us = sum(evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)) * 1e3 / args.steps
+    flops = 2.0 * M * spec.N * spec.K
+    nbytes = w4a16_bytes(M, spec.K, spec.N)
+    achieved = nbytes / (launch_us * 1e-6) / 1e9
+    kname = f"gemm_w4a16_{spec.name}"
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_for(kname, args.workload),
+                "kernel": kname, "bytes_per_launch": nbytes, "avg_launch_us": round(launch_us, 2),
+                "weight_copies": copies}
+    breakdown = {spec.name: {"gemm_us": round(launch_us, 2), "GBps": round(achieved, 1),
+                             "gemm_TFLOPs": round(flops / (launch_us * 1e-6) / 1e12, 3)}}
+    return dict(value=flops / (ms_per_step * 1e-3) / 1e12, ms_per_step=ms_per_step, gpu_ms_per_step=None,
+                roofline=roofline, breakdown=breakdown, specs=[spec], fmt="bf16", fused=None)
+
+
+def cpu_baseline_w4a16(spec):
+    """The W4A16 oracle, as it stands, on the whole workload (quantize W, fp64
+    product): about 10 s of host time."""
+    import synth
+    from oracle import w4a16 as W
+
+    d = synth.draw_w4a16(spec)
+    threads = _blas_threads()
+    t0 = time.perf_counter()
+    W.forward(d["X"], d["W"], d["b"])
+    secs = time.perf_counter() - t0
+    return {"value": round(2.0 * spec.M * spec.N * spec.K / secs / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{spec.name}: all {spec.M} tokens x {spec.N} outputs (K={spec.K}); {secs:.1f} s of oracle "
+                      "time (INT4 weight quantization, fp64 product, bias); quantization is single-threaded "
+                      f"numpy, the product uses {threads} BLAS threads"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover - optional dependency
+        return 1
+
+
 def fused_qkv(args, sq, synth, torch, np, layer, w, x, ws, out, epi, M, flops):
     """The QKV layer with the Q/K RMS normalization and rotary embedding in the
     GEMM epilogue (svdq_gemm_qkv), same inputs and step count."""
@@ -256,11 +360,7 @@ def cpu_baseline(specs, budget_rows=512):
     import synth
     from oracle import layer as Ly
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - optional dependency
-        threads = 1
+    threads = _blas_threads()
     work, secs, parts = 0.0, 0.0, []
     for spec in specs:
         L = synth.draw_layer(spec)
@@ -288,23 +388,27 @@ def main():
               "a single GPU (token-parallel sharding needs no collective, so N GPUs are N copies of "
               "this measurement).", file=sys.stderr)
         sys.exit(2)
-    r = gpu_leg(args)
+    w4a16 = args.workload in W4A16
+    r = gpu_leg_w4a16(args) if w4a16 else gpu_leg(args)
     specs = r["specs"]
     cfg = {"workload": args.workload, "layers": [
         {"name": s.name, "M": s.M, "K": s.K, "N": s.N, "rank": s.rank + s.lora_rank, "fmt": s.fmt,
-         "epilogue": "lowrank+bias" + ("+gelu" if s.gelu else "")} for s in specs],
+         "epilogue": "bias" if w4a16 else "lowrank+bias" + ("+gelu" if s.gelu else "")} for s in specs],
         "output": "bf16", "weights": "packed once before timing"}
+    if w4a16:
+        cfg["activations"] = "bf16 (W4A16)"
     line = {
         "metric": METRIC, "value": round(r["value"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": r["fmt"], "data": "synthetic",
         "config": cfg, "roofline": r["roofline"], "breakdown": r["breakdown"],
-        "gpu_ms_per_step": round(r["gpu_ms_per_step"], 4),
     }
+    if r["gpu_ms_per_step"] is not None:
+        line["gpu_ms_per_step"] = round(r["gpu_ms_per_step"], 4)
     if r["fused"] is not None:
         line["fused_mlp" if args.workload == "mlp_mxfp4" else "fused_qkv"] = r["fused"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(specs)
+        line["cpu_baseline"] = cpu_baseline_w4a16(specs[0]) if w4a16 else cpu_baseline(specs)
     print(json.dumps(line), flush=True)
 
 

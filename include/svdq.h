@@ -166,6 +166,24 @@ svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const 
                           uint32_t epi, int32_t head_dim, const uint16_t* norm_q, const uint16_t* norm_k, float eps,
                           const float* rope_cos, const float* rope_sin, void* Y, int64_t ldy, void* stream);
 
+/* 4-bit weights with 16-bit activations (W4A16), the Nunchaku in Diffusers page,
+ * section "Introducing Nunchaku Lite": the memory-bound modulation projections
+ * keep bf16 inputs and read INT4 weights.  One launch computes
+ *     Y = X deQ(Q4(W))^T (+ b),  fp32 sums of exact bf16 products,
+ * Y written as bf16 (nearest even), or float32 with SVDQ_EPI_OUT_F32.  The weights
+ * are an INT4-g64, rank-0 blob from svdq_pack_weight with R = W; its lambda is not
+ * applied (an AWQ-style per-channel scale is folded into W and the previous
+ * operation, so pack with lambda = 1).  The kernel is built for few tokens (it
+ * streams all weights once per 16 tokens); any M is computed correctly.
+ *   X  device, bf16 bits, M x K, row stride ldx (K <= ldx <= 2^24, multiple of 8),
+ *      16-byte aligned
+ *   Y  device, M x N, row stride ldy (>= N, multiple of 8), 16-byte aligned
+ *   epi  SVDQ_EPI_BIAS and / or SVDQ_EPI_OUT_F32
+ * d->fmt other than SVDQ_INT4_G64, d->rank != 0 or other epilogue flags give
+ * SVDQ_ERR_FORMAT; other checks and errors as svdq_gemm. */
+svdq_status svdq_gemm_w4a16(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M,
+                            int64_t ldx, void* Y, int64_t ldy, uint32_t epi, void* stream);
+
 /* Both launches; workspace >= svdq_act_bytes(d, M) bytes (device, 256-aligned). */
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
                         int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi,

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 102
+    assert L.svdq_version() == 103
     for s in range(8):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -149,6 +149,27 @@ def test_gemm_qkv_validation(L, forced_device_error):
     assert f(ctypes.byref(D(fmt=2, K=1024, N=768)), *ok) == 3                                 # INT4
     assert f(d, P, P, 4, 3, 128, P + 8, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 4   # norm_q aligned
     assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P + 8, 768, None) == 4   # Y aligned
+
+
+def test_gemm_w4a16_validation(L, forced_device_error):
+    f = L.svdq_gemm_w4a16
+    d = ctypes.byref(D(fmt=2, K=1024, N=512, rank=0))
+    assert f(d, P, P, 4, 1024, P, 512, 10, None) == 6         # valid (bias, fp32 out) -> device check
+    assert f(d, P, None, 0, 1024, None, 512, 2, None) == 6    # M = 0: X and Y may be NULL
+    assert f(None, P, P, 4, 1024, P, 512, 2, None) == 1
+    assert f(d, P, None, 4, 1024, P, 512, 2, None) == 1
+    assert f(d, P, P, 4, 1000, P, 512, 2, None) == 2          # ldx < K
+    assert f(d, P, P, 4, 1024, P, 500, 2, None) == 2          # ldy < N
+    assert f(d, P, P, 4, (1 << 24) + 8, P, 512, 2, None) == 2  # ldx beyond 2^24
+    assert f(ctypes.byref(D(fmt=2, K=1000, N=512, rank=0)), P, P, 4, 1024, P, 512, 2, None) == 2
+    assert f(ctypes.byref(D(fmt=1, K=1024, N=512, rank=0)), P, P, 4, 1024, P, 512, 2, None) == 3  # MXFP4
+    assert f(ctypes.byref(D(fmt=2, K=1024, N=512, rank=16)), P, P, 4, 1024, P, 512, 2, None) == 3  # rank
+    assert f(d, P, P, 4, 1024, P, 512, 1, None) == 3          # low-rank flag
+    assert f(d, P, P, 4, 1024, P, 512, 6, None) == 3          # GELU flag
+    assert f(d, P, P + 8, 4, 1024, P, 512, 2, None) == 4      # X aligned
+    assert f(d, P, P, 4, 1028, P, 512, 2, None) == 4          # ldx multiple of 8
+    assert f(d, P, P, 4, 1024, P + 8, 512, 2, None) == 4      # Y aligned
+    assert f(d, P + 64, P, 4, 1024, P, 512, 2, None) == 4     # blob 256-aligned
 
 
 def test_unpack_validation(L, forced_device_error):

@@ -133,6 +133,21 @@ def gemm_qkv(layer: Layer, w_packed, a_packed, M: int, epi: int, norm_q, norm_k,
     return out
 
 
+def gemm_w4a16(layer: Layer, w_packed, X, epi: int = 0, out=None, stream=None):
+    """W4A16: Y = X deQ(Q4(W))^T (+ b) for an INT4 rank-0 blob and bf16 X (M x K);
+    returns Y (M x N, bf16, or float32 with EPI_OUT_F32)."""
+    torch = _torch()
+    d, p = _desc_ref(layer)
+    M = X.shape[0]
+    if out is None:
+        dt = torch.float32 if epi & EPI_OUT_F32 else torch.bfloat16
+        out = torch.empty((M, layer.N), dtype=dt, device=X.device)
+    st = lib().svdq_gemm_w4a16(p, _ptr(w_packed), _ptr(X), M, X.stride(0), _ptr(out), out.stride(0), epi,
+                               _stream(stream))
+    check("svdq_gemm_w4a16", st)
+    return out
+
+
 def linear(layer: Layer, w_packed, X, epi: int, out=None, workspace=None, stream=None):
     """Both launches: Y = act(deQ(Q(X/lam)) deQ(Q(R))^T + (X/lam L1) L2 + b)."""
     torch = _torch()

@@ -29,6 +29,7 @@ SIGNATURES = {
     "svdq_gemm_quant": (ctypes.c_int, [_D, _P, _P, _I64, ctypes.c_uint32, _D, _P, _P, _P]),
     "svdq_gemm_qkv": (ctypes.c_int, [_D, _P, _P, _I64, ctypes.c_uint32, ctypes.c_int32, _P, _P, ctypes.c_float,
                                      _P, _P, _P, _I64, _P]),
+    "svdq_gemm_w4a16": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _I64, ctypes.c_uint32, _P]),
     "svdq_linear": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _I64, ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
     "svdq_unpack_weight": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "svdq_unpack_act": (ctypes.c_int, [_D, _P, _I64, _P, _P, _P, _P]),

@@ -27,6 +27,8 @@ hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const u
                            int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, const uint16_t* norm_q,
                            const uint16_t* norm_k, float eps, const float* rope_cos, const float* rope_sin,
                            hipStream_t s);
+hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K, int N, const uint16_t* X,
+                             int64_t ldx, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s);
 hipError_t launch_unpack_weight(int fmt, int K, int N, int rank, const WeightLayout& wl, const uint8_t* blob,
                                 uint8_t* codes, void* scales, uint16_t* L1, uint16_t* L2, float* lam, uint16_t* bias,
                                 hipStream_t s);
@@ -41,6 +43,7 @@ namespace {
 constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int kGemmQuantMaxRank = 64;   // next layer's rank in svdq_gemm_quant (4 rank tiles of 16)
 constexpr int kQkvHeadDim = 128;        // svdq_gemm_qkv: one head per 128 output columns of a wave
+constexpr int64_t kW4A16MaxLdx = int64_t(1) << 24;   // svdq_gemm_w4a16: 16 rows of X within a 32-bit buffer range
 constexpr uint32_t kEpiAll = SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU | SVDQ_EPI_OUT_F32;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -107,7 +110,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 102; }
+int svdq_version(void) { return 103; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -234,6 +237,24 @@ svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const 
   return launched(launch_gemm_qkv(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                   al, d->K, d->N, M, Y, ldy, epi, norm_q, norm_k, eps, rope_cos, rope_sin,
                                   static_cast<hipStream_t>(stream)));
+}
+
+svdq_status svdq_gemm_w4a16(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M,
+                            int64_t ldx, void* Y, int64_t ldy, uint32_t epi, void* stream) {
+  if (!d || !w_packed || (M > 0 && (!X || !Y))) return SVDQ_ERR_NULL;
+  svdq_status s = check_shape(d);
+  if (s != SVDQ_OK) return s;
+  if (M < 0 || M > kMaxRows || ldx < d->K || ldx > kW4A16MaxLdx || ldy < d->N) return SVDQ_ERR_SHAPE;
+  if ((s = check_fmt(d)) != SVDQ_OK) return s;
+  if (d->fmt != SVDQ_INT4_G64 || d->rank != 0 || (epi & ~(SVDQ_EPI_BIAS | SVDQ_EPI_OUT_F32)) != 0)
+    return SVDQ_ERR_FORMAT;
+  if (!aligned(w_packed, 256) || (M > 0 && (!aligned(X, 16) || !aligned(Y, 16))) || ldx % 8 != 0 || ldy % 8 != 0)
+    return SVDQ_ERR_ALIGN;
+  if ((s = device_check()) != SVDQ_OK) return s;
+  if (M == 0) return SVDQ_OK;
+  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  return launched(launch_gemm_w4a16(static_cast<const uint8_t*>(w_packed), wl, d->K, d->N, X, ldx, M, Y, ldy, epi,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M, int64_t ldx,

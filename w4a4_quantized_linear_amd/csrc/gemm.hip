@@ -741,6 +741,184 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
 }
 
+// ------------------------------------------------------------------ W4A16
+//
+// The second kernel family of the Nunchaku in Diffusers page (section
+// "Introducing Nunchaku Lite"): 4-bit weights with 16-bit activations for the
+// memory-bound modulation projections, Y = X deQ(Q4(W))^T + b with X in bf16.
+// The weights use the INT4-g64 packing of the W4A4 layer.  A workgroup computes
+// T 16-row weight tiles for up to 16 tokens at a time on the bf16 MFMA
+// (16 x 16 x 32, weights as A); its four waves take every fourth 128-K step and
+// their fp32 sums are added in wave order through LDS.  A code q becomes the
+// bf16 128 + u with u = q + 8 (the offset nibble in the mantissa of 128, one
+// byte permute per two codes); a second product of the same X with the bf16
+// constant -136 goes into the same accumulator, so each 64-group's sum is the
+// exact sum of q x in fp32 before its scale is applied.  Each wave keeps the
+// codes and scales of its next kW4A16Depth steps and the X of its next two in
+// flight.  All loads are buffer loads (scalar base and step offset, one
+// per-lane offset each); X rows past M fall outside the X range and read 0.
+struct W4A16Args {
+  const uint8_t* wblob;
+  size_t w_codes, w_scales, w_bias;
+  const uint16_t* X;
+  int64_t ldx, M, N_pad, ldy;
+  int K;
+  uint32_t epi;
+  void* Y;
+};
+
+// 8 INT4 codes in the packed dword order (code e in byte e % 4, high nibble for
+// e >= 4) -> 4 dwords of bf16 pairs 128 + q + 8 in code order.  k43 holds 0x43
+// in every byte (the high byte of bf16 128).
+__device__ __forceinline__ uint4 w4_to_bf16(uint32_t d, uint32_t k43) {
+  d ^= 0x88888888u;                                // offset nibbles u = q + 8
+  const uint32_t lo = d & 0x0F0F0F0Fu;             // codes 0..3, one per byte
+  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;      // codes 4..7
+  // selector bytes 0..3 pick bytes of the code word, 4 picks 0x43
+  return make_uint4(__builtin_amdgcn_perm(k43, lo, 0x04010400u), __builtin_amdgcn_perm(k43, lo, 0x04030402u),
+                    __builtin_amdgcn_perm(k43, hi, 0x04010400u), __builtin_amdgcn_perm(k43, hi, 0x04030402u));
+}
+
+constexpr int kW4A16Depth = 4;   // 128-K steps of codes and scales in flight per wave
+
+template <int T, bool OUT_F32>
+__global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
+  __shared__ v4f red[3][T][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KS = a.K / kKStep, n = KS / 4;         // this wave's steps: ks = w + 4 i
+  const int c = lane >> 4, tl = lane & 15;
+  const int64_t row0 = int64_t(blockIdx.x) * 16 * T;
+  // codes of the T tiles (KS KiB each), scales of all steps for rows row0 ..
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(a.wblob + a.w_codes + size_t(row0 / 16) * KS * 1024, uint32_t(T * KS * 1024));
+  const __amdgpu_buffer_rsrc_t rS =
+      make_rsrc(a.wblob + a.w_scales + size_t(row0) * 4, uint32_t((size_t(KS - 1) * a.N_pad + 16 * T) * 4));
+  const uint32_t wvoff = uint32_t(lane) * 16, svoff = uint32_t(c) * 16;
+  const uint4 m136 = make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u);  // bf16 -136
+  // an opaque copy keeps the constant in a register for the byte permutes
+  uint32_t k43 = 0x43434343u;
+  asm volatile("" : "+v"(k43));
+  float bias[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    bias[t][0] = bias[t][1] = bias[t][2] = bias[t][3] = 0.f;
+    if (a.epi & SVDQ_EPI_BIAS) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.wblob + a.w_bias) + row0 +
+                                                       t * 16 + c * 4);
+      bias[t][0] = bf_lo(bb.x); bias[t][1] = bf_hi(bb.x); bias[t][2] = bf_lo(bb.y); bias[t][3] = bf_hi(bb.y);
+    }
+  }
+  struct WStage { uint4 q[T], s[T]; };
+
+  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+    const int64_t rows = a.M - m0 < 16 ? a.M - m0 : 16;
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + m0 * a.ldx, uint32_t(rows * a.ldx * 2));
+    const uint32_t xvoff = (uint32_t(tl) * uint32_t(a.ldx) + uint32_t(c) * 16) * 2;
+    // loads past the last step repeat it (cache hits, never used)
+    auto loadw = [&](int i, WStage& st) {
+      i = i < n ? i : n - 1;
+      const int ks = w + 4 * i;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        st.q[t] = load_frag(rW, wvoff, uint32_t((t * KS + ks) * 1024));
+        st.s[t] = load_frag(rS, svoff, uint32_t((size_t(ks) * a.N_pad + t * 16) * 4));
+      }
+    };
+    auto loadx = [&](int i, uint4 (&x)[4]) {
+      i = i < n ? i : n - 1;
+      const uint32_t so = uint32_t(w + 4 * i) * kKStep * 2;
+      // MFMA j covers group j / 2, half j % 2 of the lane's 16 codes per group
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = load_frag(rX, xvoff + (j >> 1) * 128 + (j & 1) * 16, so);
+    };
+    v4f acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const WStage& st, const uint4 (&x)[4]) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t q0 = g == 0 ? st.q[t].x : st.q[t].z, q1 = g == 0 ? st.q[t].y : st.q[t].w;
+          v4f p = {0.f, 0.f, 0.f, 0.f};
+          p = mfma_bf16(w4_to_bf16(q0, k43), x[2 * g], p);
+          p = mfma_bf16(w4_to_bf16(q1, k43), x[2 * g + 1], p);
+          p = mfma_bf16(m136, x[2 * g], p);
+          p = mfma_bf16(m136, x[2 * g + 1], p);
+          const uint32_t sd[4] = {st.s[t].x, st.s[t].y, st.s[t].z, st.s[t].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(h2f(g == 0 ? sd[e] : sd[e] >> 16), p[e], acc[t][e]);
+        }
+      }
+    };
+    WStage ws[kW4A16Depth];
+    uint4 xs[2][4];
+#pragma unroll
+    for (int j = 0; j < kW4A16Depth; ++j) loadw(j, ws[j]);
+    loadx(0, xs[0]);
+    loadx(1, xs[1]);
+    for (int i0 = 0; i0 < n; i0 += kW4A16Depth) {
+#pragma unroll
+      for (int j = 0; j < kW4A16Depth; ++j) {
+        if (i0 + j < n) compute(ws[j], xs[j & 1]);
+        loadw(i0 + j + kW4A16Depth, ws[j]);
+        loadx(i0 + j + 2, xs[j & 1]);
+      }
+    }
+    // wave sums in order 0 + 1 + 2 + 3; lane holds rows row0 + 16 t + 4 c .. + 3 of token m0 + tl
+    if (w > 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) red[w - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (w == 0 && tl < rows) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const v4f a1 = red[0][t][lane], a2 = red[1][t][lane], a3 = red[2][t][lane];
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = ((acc[t][e] + a1[e]) + a2[e]) + a3[e] + bias[t][e];
+        const int64_t o = (m0 + tl) * a.ldy + row0 + t * 16 + c * 4;
+        if (OUT_F32)
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + o) = make_float4(y[0], y[1], y[2], y[3]);
+        else
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.Y) + o) =
+              make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Requires K % 512 == 0, N % 16 == 0, X rows 16-byte aligned with 16 ldx * 2
+// bytes below 2^32, Y rows 16-byte aligned.  One workgroup per 32 rows of N
+// (16 when N is not a multiple of 32).
+hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K, int N, const uint16_t* X,
+                             int64_t ldx, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
+  W4A16Args a{};
+  a.wblob = wblob;
+  a.w_codes = wl.codes; a.w_scales = wl.scales; a.w_bias = wl.bias;
+  a.X = X; a.ldx = ldx; a.M = M; a.N_pad = wl.N_pad; a.ldy = ldy;
+  a.K = K; a.epi = epi; a.Y = Y;
+  const bool f32 = (epi & SVDQ_EPI_OUT_F32) != 0;
+  const dim3 block(256);
+  if (N % 32 == 0) {
+    const dim3 grid(unsigned(N / 32));
+    if (f32)
+      hipLaunchKernelGGL((gemm_w4a16_kernel<2, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_w4a16_kernel<2, false>), grid, block, 0, s, a);
+  } else {
+    const dim3 grid(unsigned(N / 16));
+    if (f32)
+      hipLaunchKernelGGL((gemm_w4a16_kernel<1, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_w4a16_kernel<1, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launcher
 
 constexpr unsigned kMinBigTiles = 128;   // MXFP4: fewer 256 x 256 tiles than this -> 128 x 128 tiles

@@ -12,8 +12,12 @@
 //   the scale of row L%16, block L/16 of the 128-K step j.
 // INT8 MFMA (v_mfma_i32_16x16x64_i8) for INT4: per 16-row x 128-K tile, lane L
 //   holds row L%16 and, for both 64-element groups g of the tile, the 16 codes
-//   at group offset (L/16)*16: bytes [8g, 8g+8) = 16 nibbles.  Scales: per 128-K
-//   step and row, two fp16 (groups 0 and 1) in 4 bytes, rows contiguous.
+//   at group offset (L/16)*16: bytes [8g, 8g+8) = 16 nibbles, two dwords of 8
+//   codes each.  Inside a dword, code e (0..7) is in byte e%4, low nibble for
+//   e < 4: masking the low (high) nibbles gives codes 0-3 (4-7) one per byte, in
+//   order, which is what both the int8 expansion and the bf16 conversion of the
+//   W4A16 kernel want.  Scales: per 128-K step and row, two fp16 (groups 0 and
+//   1) in 4 bytes, rows contiguous.
 // bf16 MFMA (v_mfma_f32_16x16x32_bf16) fragments for the low-rank branch: lane
 //   L holds row/column L%16 and 8 consecutive K (rank) elements at (L/16)*8.
 //
@@ -131,9 +135,9 @@ __host__ __device__ inline size_t code_byte(int fmt, int64_t row, int k, int K, 
     *hi = t & 1;
     return code_chunk(rt, ks, K, blk * 16 + r) + t / 2;
   }
-  const int g = kk / 64, o = kk % 64, c = o / 16, t = o % 16;
-  *hi = t & 1;
-  return code_chunk(rt, ks, K, c * 16 + r) + g * 8 + t / 2;
+  const int g = kk / 64, o = kk % 64, c = o / 16, t = o % 16, e = t % 8;
+  *hi = e >> 2;
+  return code_chunk(rt, ks, K, c * 16 + r) + g * 8 + (t / 8) * 4 + (e & 3);
 }
 
 // ---- scales ----

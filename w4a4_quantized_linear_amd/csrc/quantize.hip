@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
             float t = x[8 * h + e] / s;
             t = __builtin_rintf(fminf(fmaxf(t, -8.0f), 7.0f));
             const int q = (s == 0.0f) ? 0 : int(t);
-            cw |= (uint32_t(q) & 0xFu) << (4 * e);
+            cw |= (uint32_t(q) & 0xFu) << (8 * (e & 3) + 4 * (e >> 2));  // INT4 dword order
           }
           const int jb = 2 * p + h;
           const int kk = (jb & 3) * 32 + c * 8;  // offset inside the 128-K step
@@ -284,7 +284,7 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
         for (int e = 0; e < 8; ++e) {
           const float tq = __builtin_rintf(fminf(fmaxf(t[e], -8.0f), 7.0f));
           const int q = (sc == 0.0f) ? 0 : int(tq);
-          cw |= (uint32_t(q) & 0xFu) << (4 * e);
+          cw |= (uint32_t(q) & 0xFu) << (8 * (e & 3) + 4 * (e >> 2));  // INT4 dword order
         }
         // group offset o = 32h + 8c: lane chunk (o / 16) * 16 + row, bytes 8 gi + (o % 16) / 2
         __builtin_amdgcn_raw_buffer_store_b32(cw, rC, uint32_t((c / 2) * 256 + row * 16 + (c % 2) * 4),
