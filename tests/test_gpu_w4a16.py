@@ -26,13 +26,17 @@ pytestmark = pytest.mark.gpu
 
 # (M, K, N, seed): one token, the modulation batch, a ragged second 16-token
 # block, an odd number of 128-K steps per wave (K = 1536: three), N not a
-# multiple of 256, a single 16-row tile, and many token blocks
+# multiple of 32 (16-row workgroups) or of 256, a single 16-row tile, many token
+# blocks, and the largest M whose X fits the kernel's LDS copy at K = 3072 (6)
+# next to the smallest that does not (7)
 CASES = [
     (1, 512, 16, 1),
     (2, 3072, 272, 2),
     (17, 1536, 512, 3),
     (40, 1024, 1040, 4),
     (300, 512, 256, 5),
+    (6, 3072, 544, 6),
+    (7, 3072, 256, 7),
 ]
 
 
@@ -118,6 +122,8 @@ def test_w4a16_no_bias_and_exact_integers(torch_dev):
     _run_and_check(torch, dev, X, Wn, None, "exact, no bias", exact=True)
     b = synth.bf16_bits_from_f32((rng.integers(-64, 65, N) * 2.0 ** -6).astype(np.float32))
     _run_and_check(torch, dev, X, Wn, b, "exact, bias", exact=True)
+    # few tokens: X read from the kernel's LDS copy
+    _run_and_check(torch, dev, np.ascontiguousarray(X[:5]), Wn, b, "exact, bias, 5 tokens", exact=True)
 
 
 def test_w4a16_zero_tokens(torch_dev):

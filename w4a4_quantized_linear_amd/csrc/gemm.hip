@@ -747,16 +747,21 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
 // "Introducing Nunchaku Lite"): 4-bit weights with 16-bit activations for the
 // memory-bound modulation projections, Y = X deQ(Q4(W))^T + b with X in bf16.
 // The weights use the INT4-g64 packing of the W4A4 layer.  A workgroup computes
-// T 16-row weight tiles for up to 16 tokens at a time on the bf16 MFMA
-// (16 x 16 x 32, weights as A); its four waves take every fourth 128-K step and
-// their fp32 sums are added in wave order through LDS.  A code q becomes the
-// bf16 128 + u with u = q + 8 (the offset nibble in the mantissa of 128, one
-// byte permute per two codes); a second product of the same X with the bf16
+// T 16-row weight tiles on the bf16 MFMA (16 x 16 x 32, weights as A, up to 16
+// tokens as B); its four waves take every fourth 128-K step and their fp32
+// sums are added in wave order through LDS.  A code q becomes the bf16
+// 128 + u with u = q + 8 (the offset nibble in the mantissa of 128, one byte
+// permute per two codes); a second product of the same X with the bf16
 // constant -136 goes into the same accumulator, so each 64-group's sum is the
 // exact sum of q x in fp32 before its scale is applied.  Each wave keeps the
-// codes and scales of its next kW4A16Depth steps and the X of its next two in
-// flight.  All loads are buffer loads (scalar base and step offset, one
-// per-lane offset each); X rows past M fall outside the X range and read 0.
+// codes and scales of its next kW4A16Depth steps in flight (buffer loads: a
+// scalar base and step offset, one per-lane offset).
+//
+// X: with XL, all M rows of X are copied once into LDS (direct-to-LDS loads,
+// issued before the first weights) and the B fragments are read from there;
+// otherwise each 16-token block's fragments are loaded from global memory two
+// steps ahead.  Token columns past M hold the last token's values (MFMA output
+// columns are independent, and those columns are never stored).
 struct W4A16Args {
   const uint8_t* wblob;
   size_t w_codes, w_scales, w_bias;
@@ -779,17 +784,22 @@ __device__ __forceinline__ uint4 w4_to_bf16(uint32_t d, uint32_t k43) {
                     __builtin_amdgcn_perm(k43, hi, 0x04010400u), __builtin_amdgcn_perm(k43, hi, 0x04030402u));
 }
 
-constexpr int kW4A16Depth = 4;   // 128-K steps of codes and scales in flight per wave
+constexpr int kW4A16Depth = 3;        // 128-K steps of codes and scales in flight per wave
+constexpr int kW4A16XLds = 40960;     // LDS for X rows (XL form): M (K * 2 + 16) bytes at most
+constexpr int kW4A16Tiles = 2;        // 16-row tiles per workgroup (when N allows)
 
-template <int T, bool OUT_F32>
+__host__ __device__ inline int w4a16_xstride(int K) { return K * 2 + 16; }   // bytes; 16 skews the banks
+
+template <int T, bool XL, bool OUT_F32>
 __global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
   __shared__ v4f red[3][T][64];
+  extern __shared__ uint4 xlds[];                  // XL: M rows of X, stride w4a16_xstride(K) bytes
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KS = a.K / kKStep, n = KS / 4;         // this wave's steps: ks = w + 4 i
   const int c = lane >> 4, tl = lane & 15;
   const int64_t row0 = int64_t(blockIdx.x) * 16 * T;
-  // codes of the T tiles (KS KiB each), scales of all steps for rows row0 ..
+  // codes of the T tiles (contiguous, KS KiB each), scales of rows row0 .. row0 + 16 T - 1
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(a.wblob + a.w_codes + size_t(row0 / 16) * KS * 1024, uint32_t(T * KS * 1024));
   const __amdgpu_buffer_rsrc_t rS =
@@ -799,74 +809,86 @@ __global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
   // an opaque copy keeps the constant in a register for the byte permutes
   uint32_t k43 = 0x43434343u;
   asm volatile("" : "+v"(k43));
-  float bias[T][4];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    bias[t][0] = bias[t][1] = bias[t][2] = bias[t][3] = 0.f;
-    if (a.epi & SVDQ_EPI_BIAS) {
-      const uint2 bb = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.wblob + a.w_bias) + row0 +
-                                                       t * 16 + c * 4);
-      bias[t][0] = bf_lo(bb.x); bias[t][1] = bf_hi(bb.x); bias[t][2] = bf_lo(bb.y); bias[t][3] = bf_hi(bb.y);
-    }
-  }
-  struct WStage { uint4 q[T], s[T]; };
 
-  for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
-    const int64_t rows = a.M - m0 < 16 ? a.M - m0 : 16;
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + m0 * a.ldx, uint32_t(rows * a.ldx * 2));
-    const uint32_t xvoff = (uint32_t(tl) * uint32_t(a.ldx) + uint32_t(c) * 16) * 2;
-    // loads past the last step repeat it (cache hits, never used)
-    auto loadw = [&](int i, WStage& st) {
-      i = i < n ? i : n - 1;
-      const int ks = w + 4 * i;
+  // bias bits first: every later wait on the vector-memory counter covers this load
+  uint2 bias_bits[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    bias_bits[t] = (a.epi & SVDQ_EPI_BIAS)
+                       ? *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.wblob + a.w_bias) +
+                                                         row0 + t * 16 + c * 4)
+                       : make_uint2(0u, 0u);
+  struct WStage { uint4 q[T], s[T]; };
+  // loads past the last step repeat it (cache hits, never used)
+  auto loadw = [&](int i, WStage& st) {
+    i = i < n ? i : n - 1;
+    const int ks = w + 4 * i;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      st.q[t] = load_frag(rW, wvoff, uint32_t((t * KS + ks) * 1024));
+      st.s[t] = load_frag(rS, svoff, uint32_t((size_t(ks) * a.N_pad + t * 16) * 4));
+    }
+  };
+  v4f acc[T];
+  auto compute = [&](const WStage& st, const uint4 (&x)[4]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        st.q[t] = load_frag(rW, wvoff, uint32_t((t * KS + ks) * 1024));
-        st.s[t] = load_frag(rS, svoff, uint32_t((size_t(ks) * a.N_pad + t * 16) * 4));
+        const uint32_t q0 = g == 0 ? st.q[t].x : st.q[t].z, q1 = g == 0 ? st.q[t].y : st.q[t].w;
+        v4f p = {0.f, 0.f, 0.f, 0.f};
+        p = mfma_bf16(w4_to_bf16(q0, k43), x[2 * g], p);
+        p = mfma_bf16(w4_to_bf16(q1, k43), x[2 * g + 1], p);
+        p = mfma_bf16(m136, x[2 * g], p);
+        p = mfma_bf16(m136, x[2 * g + 1], p);
+        const uint32_t sd[4] = {st.s[t].x, st.s[t].y, st.s[t].z, st.s[t].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(h2f(g == 0 ? sd[e] : sd[e] >> 16), p[e], acc[t][e]);
       }
-    };
-    auto loadx = [&](int i, uint4 (&x)[4]) {
-      i = i < n ? i : n - 1;
-      const uint32_t so = uint32_t(w + 4 * i) * kKStep * 2;
-      // MFMA j covers group j / 2, half j % 2 of the lane's 16 codes per group
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = load_frag(rX, xvoff + (j >> 1) * 128 + (j & 1) * 16, so);
-    };
-    v4f acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const WStage& st, const uint4 (&x)[4]) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const uint32_t q0 = g == 0 ? st.q[t].x : st.q[t].z, q1 = g == 0 ? st.q[t].y : st.q[t].w;
-          v4f p = {0.f, 0.f, 0.f, 0.f};
-          p = mfma_bf16(w4_to_bf16(q0, k43), x[2 * g], p);
-          p = mfma_bf16(w4_to_bf16(q1, k43), x[2 * g + 1], p);
-          p = mfma_bf16(m136, x[2 * g], p);
-          p = mfma_bf16(m136, x[2 * g + 1], p);
-          const uint32_t sd[4] = {st.s[t].x, st.s[t].y, st.s[t].z, st.s[t].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(h2f(g == 0 ? sd[e] : sd[e] >> 16), p[e], acc[t][e]);
-        }
-      }
-    };
-    WStage ws[kW4A16Depth];
-    uint4 xs[2][4];
+    }
+  };
+  WStage ws[kW4A16Depth];
+
+  if constexpr (XL) {
+    // copy X (M rows, K * 2 bytes each) into LDS: 1 KiB pieces, wave w takes w, w + 4, ...
+    const int per_row = a.K / 512, pieces = int(a.M) * per_row, xs_b = w4a16_xstride(a.K);
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X, uint32_t(a.M * a.ldx * 2));
+    for (int pc = w; pc < pieces; pc += 4) {
+      const int r = pc / per_row, q = pc % per_row;
+      load_frag_lds(rX, reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(xlds) + r * xs_b + q * 1024), wvoff,
+                    uint32_t(r * a.ldx * 2 + q * 1024));
+    }
+    // keep every X copy ahead of the weight loads (the wait below counts on it)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kW4A16Depth; ++j) loadw(j, ws[j]);
-    loadx(0, xs[0]);
-    loadx(1, xs[1]);
+    // the X copies were issued before the 2 T kW4A16Depth weight loads
+    wait_barrier<2 * T * kW4A16Depth>();
+    const int tr = tl < a.M ? tl : int(a.M) - 1;
+    const uint8_t* const xb = reinterpret_cast<const uint8_t*>(xlds) + tr * xs_b + (w * kKStep + c * 16) * 2;
+    auto readx = [&](int i, uint4 (&x)[4]) {
+      const uint8_t* const p = xb + i * 4 * kKStep * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint4*>(p + (j >> 1) * 128 + (j & 1) * 16);
+    };
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < n; i0 += kW4A16Depth) {
 #pragma unroll
       for (int j = 0; j < kW4A16Depth; ++j) {
-        if (i0 + j < n) compute(ws[j], xs[j & 1]);
+        if (i0 + j < n) {
+          uint4 x[4];
+          readx(i0 + j, x);
+          compute(ws[j], x);
+        }
         loadw(i0 + j + kW4A16Depth, ws[j]);
-        loadx(i0 + j + 2, xs[j & 1]);
       }
     }
-    // wave sums in order 0 + 1 + 2 + 3; lane holds rows row0 + 16 t + 4 c .. + 3 of token m0 + tl
+  }
+
+  // wave sums in order 0 + 1 + 2 + 3; lane holds rows row0 + 16 t + 4 c .. + 3 of token m0 + tl
+  auto finish = [&](int64_t m0, int64_t rows) {
     if (w > 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t) red[w - 1][t][lane] = acc[t];
@@ -877,8 +899,10 @@ __global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
       for (int t = 0; t < T; ++t) {
         const v4f a1 = red[0][t][lane], a2 = red[1][t][lane], a3 = red[2][t][lane];
         float y[4];
+        const float b[4] = {bf_lo(bias_bits[t].x), bf_hi(bias_bits[t].x), bf_lo(bias_bits[t].y),
+                            bf_hi(bias_bits[t].y)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = ((acc[t][e] + a1[e]) + a2[e]) + a3[e] + bias[t][e];
+        for (int e = 0; e < 4; ++e) y[e] = ((acc[t][e] + a1[e]) + a2[e]) + a3[e] + b[e];
         const int64_t o = (m0 + tl) * a.ldy + row0 + t * 16 + c * 4;
         if (OUT_F32)
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + o) = make_float4(y[0], y[1], y[2], y[3]);
@@ -888,12 +912,46 @@ __global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
       }
     }
     __syncthreads();
+  };
+
+  if constexpr (XL) {
+    finish(0, a.M);
+  } else {
+    for (int64_t m0 = 0; m0 < a.M; m0 += 16) {
+      const int64_t rows = a.M - m0 < 16 ? a.M - m0 : 16;
+      // rows past M fall outside the X range and read 0
+      const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.X + m0 * a.ldx, uint32_t(rows * a.ldx * 2));
+      const uint32_t xvoff = (uint32_t(tl) * uint32_t(a.ldx) + uint32_t(c) * 16) * 2;
+      auto loadx = [&](int i, uint4 (&x)[4]) {
+        i = i < n ? i : n - 1;
+        const uint32_t so = uint32_t(w + 4 * i) * kKStep * 2;
+        // MFMA j covers group j / 2, half j % 2 of the lane's 16 codes per group
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = load_frag(rX, xvoff + (j >> 1) * 128 + (j & 1) * 16, so);
+      };
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+      uint4 xs[2][4];
+#pragma unroll
+      for (int j = 0; j < kW4A16Depth; ++j) loadw(j, ws[j]);
+      loadx(0, xs[0]);
+      loadx(1, xs[1]);
+      for (int i0 = 0; i0 < n; i0 += 2 * kW4A16Depth) {
+#pragma unroll
+        for (int j = 0; j < 2 * kW4A16Depth; ++j) {
+          if (i0 + j < n) compute(ws[j % kW4A16Depth], xs[j & 1]);
+          loadw(i0 + j + kW4A16Depth, ws[j % kW4A16Depth]);
+          loadx(i0 + j + 2, xs[j & 1]);
+        }
+      }
+      finish(m0, rows);
+    }
   }
 }
 
-// Requires K % 512 == 0, N % 16 == 0, X rows 16-byte aligned with 16 ldx * 2
-// bytes below 2^32, Y rows 16-byte aligned.  One workgroup per 32 rows of N
-// (16 when N is not a multiple of 32).
+// Requires K % 512 == 0, N % 16 == 0, X rows 16-byte aligned with M ldx * 2
+// bytes (XL form) or 16 ldx * 2 bytes below 2^32, Y rows 16-byte aligned.
+// One workgroup per 32 rows of N (16 when N is not a multiple of 32).
 hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K, int N, const uint16_t* X,
                              int64_t ldx, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
   W4A16Args a{};
@@ -902,20 +960,23 @@ hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K
   a.X = X; a.ldx = ldx; a.M = M; a.N_pad = wl.N_pad; a.ldy = ldy;
   a.K = K; a.epi = epi; a.Y = Y;
   const bool f32 = (epi & SVDQ_EPI_OUT_F32) != 0;
+  const bool xl = M <= 16 && M * w4a16_xstride(K) <= kW4A16XLds && M * ldx * 2 < (int64_t(1) << 32);
+  const size_t lds = xl ? size_t(M) * w4a16_xstride(K) : 0;
   const dim3 block(256);
-  if (N % 32 == 0) {
-    const dim3 grid(unsigned(N / 32));
-    if (f32)
-      hipLaunchKernelGGL((gemm_w4a16_kernel<2, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_w4a16_kernel<2, false>), grid, block, 0, s, a);
-  } else {
-    const dim3 grid(unsigned(N / 16));
-    if (f32)
-      hipLaunchKernelGGL((gemm_w4a16_kernel<1, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_w4a16_kernel<1, false>), grid, block, 0, s, a);
+#define SVDQ_W4A16(T_, XL_)                                                                        \
+  {                                                                                                \
+    const dim3 grid(unsigned(N / (16 * T_)));                                                      \
+    if (f32)                                                                                       \
+      hipLaunchKernelGGL((gemm_w4a16_kernel<T_, XL_, true>), grid, block, lds, s, a);              \
+    else                                                                                           \
+      hipLaunchKernelGGL((gemm_w4a16_kernel<T_, XL_, false>), grid, block, lds, s, a);             \
   }
+  if (N % (16 * kW4A16Tiles) == 0) {
+    if (xl) SVDQ_W4A16(kW4A16Tiles, true) else SVDQ_W4A16(kW4A16Tiles, false)
+  } else {
+    if (xl) SVDQ_W4A16(1, true) else SVDQ_W4A16(1, false)
+  }
+#undef SVDQ_W4A16
   return hipGetLastError();
 }
 
