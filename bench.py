@@ -217,14 +217,10 @@ def gpu_leg_w4a16(args):
     M = spec.M
     it = [0]
 
-    def step(ev=None):
+    def step():
         w = ws[it[0] % copies]
         it[0] += 1
-        if ev is not None:
-            ev[0].record()
         sq.gemm_w4a16(layer, w, x, sq.EPI_BIAS, out=out)
-        if ev is not None:
-            ev[1].record()
 
     for _ in range(args.warmup):
         step()
@@ -236,14 +232,19 @@ def gpu_leg_w4a16(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # one launch per step, back to back on the current stream: the kernel is a
+    # few microseconds long, so events around each launch would time mostly
+    # themselves; the events bracket the whole run instead
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    launch_us = sum(evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)) * 1e3 / args.steps
+    launch_us = start.elapsed_time(stop) * 1e3 / args.steps
     flops = 2.0 * M * spec.N * spec.K
     nbytes = w4a16_bytes(M, spec.K, spec.N)
     achieved = nbytes / (launch_us * 1e-6) / 1e9

@@ -27,8 +27,9 @@ pytestmark = pytest.mark.gpu
 # (M, K, N, seed): one token, the modulation batch, a ragged second 16-token
 # block, an odd number of 128-K steps per wave (K = 1536: three), N not a
 # multiple of 32 (16-row workgroups) or of 256, a single 16-row tile, many token
-# blocks, and the largest M whose X fits the kernel's LDS copy at K = 3072 (6)
-# next to the smallest that does not (7)
+# blocks, the largest M whose X fits the kernel's LDS copy at K = 3072 (6) next
+# to the smallest that does not (7), and a wide layer whose workgroups take two
+# 16-row tiles (X from global memory, N / 32 >= 512)
 CASES = [
     (1, 512, 16, 1),
     (2, 3072, 272, 2),
@@ -37,6 +38,7 @@ CASES = [
     (300, 512, 256, 5),
     (6, 3072, 544, 6),
     (7, 3072, 256, 7),
+    (17, 512, 16384, 8),
 ]
 
 

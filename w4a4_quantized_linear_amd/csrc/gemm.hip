@@ -951,7 +951,6 @@ __global__ void __launch_bounds__(256, 3) gemm_w4a16_kernel(W4A16Args a) {
 
 // Requires K % 512 == 0, N % 16 == 0, X rows 16-byte aligned with M ldx * 2
 // bytes (XL form) or 16 ldx * 2 bytes below 2^32, Y rows 16-byte aligned.
-// One workgroup per 32 rows of N (16 when N is not a multiple of 32).
 hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K, int N, const uint16_t* X,
                              int64_t ldx, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
   W4A16Args a{};
@@ -971,11 +970,15 @@ hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K
     else                                                                                           \
       hipLaunchKernelGGL((gemm_w4a16_kernel<T_, XL_, false>), grid, block, lds, s, a);             \
   }
-  if (N % (16 * kW4A16Tiles) == 0) {
-    if (xl) SVDQ_W4A16(kW4A16Tiles, true) else SVDQ_W4A16(kW4A16Tiles, false)
-  } else {
-    if (xl) SVDQ_W4A16(1, true) else SVDQ_W4A16(1, false)
-  }
+  // X from LDS: one 16-row tile per workgroup (the most workgroups in flight).
+  // X from global memory: two tiles share each X fragment, when that still
+  // leaves at least two workgroups per CU.
+  if (xl)
+    SVDQ_W4A16(1, true)
+  else if (N % (16 * kW4A16Tiles) == 0 && N / (16 * kW4A16Tiles) >= 512)
+    SVDQ_W4A16(kW4A16Tiles, false)
+  else
+    SVDQ_W4A16(1, false)
 #undef SVDQ_W4A16
   return hipGetLastError();
 }
