@@ -9,13 +9,15 @@ What it computes, step by step in the order and notation of the pages
 (SVDQuant notes page, hoonably.github.io/blog/svdquant; "Nunchaku 4-bit
 diffusion inference in Diffusers" page; SVDQuant abstract, arXiv 2411.05007):
 
-* formats.py   -- rounding to bf16 / fp16 / fp32 and the E2M1 and E8M0
+* formats.py   -- rounding to bf16 / fp16 / fp32 and the E2M1, E8M0 and E4M3
                   number formats (format definitions; the FP4 maximum of 6 is
                   the q_max of the notes page, section 3).
 * quant.py     -- the max-scaled symmetric quantizer of section 3 applied per
                   group along K (MXFP4: groups of 32 with a power-of-two scale;
-                  INT4: groups of 64 with an fp16 scale), dequantization and
-                  the canonical two-codes-per-byte packing.
+                  INT4: groups of 64 with an fp16 scale; NVFP4-style: groups of
+                  16 with an E4M3 scale and a float32 tensor scale, the
+                  Blackwell format the Nunchaku in Diffusers page names),
+                  dequantization and the canonical two-codes-per-byte packing.
 * decompose.py -- offline calibration: per-input-channel smoothing factors,
                   the smoothed weight, its truncated SVD (section 4.2,
                   W_hat = L1 L2 + R with L1 = U Sigma_r, L2 = V_r^T), the 16-bit

@@ -11,6 +11,10 @@ the SVDQuant notes page states in section 3, "Quantization Preliminary"):
 * E2M1 (FP4): sign bit plus 3-bit magnitude code; magnitudes
   0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7.  Largest value 6 = q_max.
 * E8M0: an unsigned byte b meaning 2^(b - 127).
+* E4M3 (OCP FP8 "E4M3FN"): sign, 4-bit exponent (bias 7), 3-bit mantissa;
+  exponent field 0 holds the subnormals m/8 * 2^-6; the largest finite
+  magnitude is 448 (exponent 15, mantissa 6); exponent 15 with mantissa 7 is
+  NaN; there is no infinity.
 
 Pinned by: tests/test_oracle_formats.py (against numpy's float16/float32
 casts and torch's bfloat16 cast, which are independent library routines,
@@ -24,6 +28,7 @@ E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.fl
 FP16_MAX = 65504.0
 BF16_MAX = float((2.0 - 2.0 ** -7) * 2.0 ** 127)
 FP32_MAX = float((2.0 - 2.0 ** -23) * 2.0 ** 127)
+E4M3_MAX = 448.0
 
 
 def round_binary(x, p: int, emin: int, max_finite: float) -> np.ndarray:
@@ -107,3 +112,31 @@ def e2m1_decode(codes) -> np.ndarray:
 
 def e8m0_value(b) -> np.ndarray:
     return np.ldexp(1.0, np.asarray(b, dtype=np.int64) - 127)
+
+
+def e4m3_value(b) -> np.ndarray:
+    """float64 value of E4M3 bytes, decoded from the fields (NaN for S.1111.111)."""
+    b = np.asarray(b, dtype=np.int64) & 0xFF
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    ex = (b >> 3) & 0xF
+    man = (b & 7).astype(np.float64)
+    val = np.where(ex == 0, np.ldexp(man / 8.0, -6), np.ldexp(1.0 + man / 8.0, ex - 7))
+    val = np.where((ex == 15) & (man == 7), np.nan, val)
+    return sign * val
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F))          # the 127 non-negative finite values, increasing
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """E4M3 byte of each non-negative value: nearest representable value, ties
+    to even (the binary rounding with 4 significand bits and minimum normal
+    exponent -6), saturating at 448."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(v < 0) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode takes non-negative values")
+    r = np.minimum(round_binary(v, 4, -6, np.inf), E4M3_MAX)
+    idx = np.searchsorted(_E4M3_POS, r)
+    if not np.array_equal(_E4M3_POS[np.minimum(idx, 126)], r):
+        raise AssertionError("e4m3_encode: rounded value not in the table")
+    return idx.astype(np.uint8)

@@ -57,9 +57,11 @@ def quantize_operands(X_bits, lam, R_nk, fmt: str) -> dict:
     """Steps 1-3: smoothed activations and both quantized operands.
     R_nk is the residual in nn.Linear orientation (N x K, float32)."""
     xhat = smooth(X_bits, lam)
+    R_nk = np.asarray(R_nk, dtype=np.float32)
+    gsR = Q.nvfp4_global_scale(R_nk) if fmt == "nvfp4" else np.float32(1.0)
     cX, sX = Q.quantize(xhat, fmt)
-    cR, sR = Q.quantize(np.asarray(R_nk, dtype=np.float32), fmt)
-    return dict(xhat=xhat, cX=cX, sX=sX, cR=cR, sR=sR)
+    cR, sR = Q.quantize(R_nk, fmt, gsR)
+    return dict(xhat=xhat, cX=cX, sX=sX, cR=cR, sR=sR, gsR=gsR)
 
 
 def down_projection(xhat: np.ndarray, L1_bits: np.ndarray) -> np.ndarray:
@@ -72,7 +74,7 @@ def forward(X_bits, lam, L1_bits, L2_bits, R_nk, b_bits, fmt: str, gelu_act: boo
     """The layer output Y_o (float64, M x N) and every intermediate."""
     ops = quantize_operands(X_bits, lam, R_nk, fmt)
     xq = Q.dequantize(ops["cX"], ops["sX"], fmt)
-    rq = Q.dequantize(ops["cR"], ops["sR"], fmt)
+    rq = Q.dequantize(ops["cR"], ops["sR"], fmt, ops["gsR"])
     y = xq @ rq.T
     if with_lowrank and L1_bits is not None and np.asarray(L1_bits).shape[1] > 0:
         D = down_projection(ops["xhat"], L1_bits)
@@ -93,11 +95,12 @@ def forward_rows(X_bits, lam, L1_bits, L2_bits, R_nk, b_bits, fmt: str, rows, co
     selected rows of X and of the N x K residual are quantized."""
     rows = np.asarray(rows)
     R_nk = np.asarray(R_nk, dtype=np.float32)
+    gsR = Q.nvfp4_global_scale(R_nk) if fmt == "nvfp4" else np.float32(1.0)   # of the whole tensor
     if cols is not None:
         cols = np.asarray(cols)
         R_nk = R_nk[cols]
-    cR, sR = Q.quantize(R_nk, fmt)
-    rq = Q.dequantize(cR, sR, fmt)
+    cR, sR = Q.quantize(R_nk, fmt, gsR)
+    rq = Q.dequantize(cR, sR, fmt, gsR)
     xhat = smooth(np.asarray(X_bits)[rows], lam)
     cX, sX = Q.quantize(xhat, fmt)
     xq = Q.dequantize(cX, sX, fmt)

@@ -20,6 +20,18 @@ Readings taken where the pages leave the step open:
   [-7, 7] is used; the notes page's worked example gives the INT4 range
   [-8, 7]), clamped to the fp16 maximum 65504.  If s == 0 every code is 0;
   otherwise q = clamp(rint(fp32(x / s)), -8, 7), rint = nearest even.
+* NVFP4-style (the Nunchaku in Diffusers page names NVFP4 as the 4-bit float
+  format of its Blackwell kernels; the format details are not on the pages,
+  so the standard two-level NVFP4 layout is taken): groups of 16 along K,
+  E2M1 codes, one E4M3 scale per group and one float32 scale gs per tensor.
+  a6 = fp32(amax / 6), u = fp32(a6 / gs), the group scale byte is the nearest
+  E4M3 value of u (ties to even, saturating at 448), S = fp32(E4M3(u) * gs),
+  and each code is the nearest E2M1 value of t = fp32(x / S) (ties to even,
+  saturating at 6, sign copied); when S == 0 every t is a zero carrying the
+  sign of x.  The residual's gs is fp32(max|R| / (6 * 448)), so the largest
+  group scale lands on 448; the activations use gs = 1 (their group scales are
+  stored directly in E4M3; smoothing has already brought X_hat to a moderate
+  range).  Dequantized value: E2M1 * E4M3 * gs.
 * All of this decision arithmetic is IEEE float32 (the division x_hat = X /
   lambda, amax / 7 and x / s are correctly rounded float32 operations).
 
@@ -37,7 +49,8 @@ import numpy as np
 
 from . import formats as F
 
-GROUP = {"mxfp4": 32, "int4": 64}
+GROUP = {"mxfp4": 32, "int4": 64, "nvfp4": 16}
+NVFP4_GLOBAL_DIV = 6.0 * 448.0          # q_max of E2M1 times the largest E4M3 value
 
 
 def _groups(x: np.ndarray, g: int) -> np.ndarray:
@@ -101,19 +114,61 @@ def int4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (codes.reshape(rows, K // 64, 64) * s[..., None]).reshape(rows, K).astype(np.float64)
 
 
-def quantize(x: np.ndarray, fmt: str):
+def nvfp4_global_scale(x: np.ndarray) -> np.float32:
+    """gs = fp32(max|x| / 2688) for a whole tensor (float32 IEEE division)."""
+    amax = np.float32(np.abs(np.asarray(x, dtype=np.float32)).max()) if np.asarray(x).size else np.float32(0)
+    return np.float32(amax / np.float32(NVFP4_GLOBAL_DIV))
+
+
+def nvfp4_quantize(x: np.ndarray, gs=1.0, row_chunk: int = 1024):
+    """x: float32 rows x K, gs: the tensor's float32 scale.  Returns (codes uint8
+    rows x K holding one E2M1 nibble each, scales uint8 rows x K/16 holding E4M3
+    bytes)."""
+    x = np.asarray(x, dtype=np.float32)
+    gs = np.float32(gs)
+    rows, K = x.shape
+    codes = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty((rows, K // 16), dtype=np.uint8)
+    for r0 in range(0, rows, row_chunk):
+        g = _groups(x[r0:r0 + row_chunk], 16)
+        amax = np.abs(g).max(axis=-1)                                   # float32
+        a6 = (amax / np.float32(6.0)).astype(np.float32)                # IEEE fp32 divide
+        with np.errstate(divide="ignore", invalid="ignore"):
+            u = (a6 / gs).astype(np.float32) if gs != 0 else np.zeros_like(a6)
+        sb = F.e4m3_encode(u.astype(np.float64))
+        S = (F.e4m3_value(sb).astype(np.float32) * gs).astype(np.float32)   # one fp32 rounding
+        with np.errstate(divide="ignore", invalid="ignore"):
+            t = np.where(S[..., None] == 0, np.float32(0) * g, g / S[..., None]).astype(np.float32)
+        codes[r0:r0 + row_chunk] = F.e2m1_encode(t.astype(np.float64)).reshape(g.shape[0], K)
+        scales[r0:r0 + row_chunk] = sb
+    return codes, scales
+
+
+def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, gs=1.0) -> np.ndarray:
+    codes = np.asarray(codes)
+    rows, K = codes.shape
+    vals = F.e2m1_decode(codes).reshape(rows, K // 16, 16)
+    return (vals * F.e4m3_value(scales)[..., None] * float(np.float32(gs))).reshape(rows, K)
+
+
+def quantize(x: np.ndarray, fmt: str, gs=1.0):
+    """Codes and scales of x; gs is the NVFP4 tensor scale (ignored otherwise)."""
     if fmt == "mxfp4":
         return mxfp4_quantize(x)
     if fmt == "int4":
         return int4_quantize(x)
+    if fmt == "nvfp4":
+        return nvfp4_quantize(x, gs)
     raise ValueError(fmt)
 
 
-def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, gs=1.0) -> np.ndarray:
     if fmt == "mxfp4":
         return mxfp4_dequantize(codes, scales)
     if fmt == "int4":
         return int4_dequantize(codes, scales)
+    if fmt == "nvfp4":
+        return nvfp4_dequantize(codes, scales, gs)
     raise ValueError(fmt)
 
 

@@ -83,7 +83,7 @@ def _pct(p: float, K: int) -> int:
 
 
 # The five workloads.  Outlier counts are round(p * K) where the recipe gives
-# a percentage.  Config 3 is a pair of layers (fc1 then fc2) in either format.
+# a percentage.  Config 3 is a pair of layers (fc1 then fc2) in each format.
 CONFIGS: Dict[str, LayerSpec] = {}
 
 
@@ -96,7 +96,7 @@ _add(LayerSpec("single", M=256, K=1024, N=1024, rank=16, fmt="int4",
 _add(LayerSpec("qkv", M=4608, K=3072, N=9216, rank=32, fmt="mxfp4",
                x_outliers=_pct(0.01, 3072), x_factor=50.0,
                w_outliers=_pct(0.01, 3072), w_kind="t3", w_factor=1.0))
-for _fmt in ("mxfp4", "int4"):
+for _fmt in ("mxfp4", "int4", "nvfp4"):
     _add(LayerSpec(f"fc1_{_fmt}", M=4608, K=3072, N=12288, rank=32, fmt=_fmt,
                    x_outliers=_pct(0.01, 3072), x_factor=50.0,
                    w_outliers=_pct(0.01, 3072), w_kind="t3", w_factor=1.0, gelu=True))
@@ -119,8 +119,8 @@ _add(LayerSpec("mod_w4a16", M=2, K=3072, N=18432, rank=0, fmt="int4",
 # Default seeds: one per workload (the workload's position in the list, 1-based;
 # the two layers of the MLP pair share seed 3 and are told apart by salt).
 SEEDS = {"single": 1, "qkv": 2, "fc1_mxfp4": 3, "fc2_mxfp4": 3, "fc1_int4": 3,
-         "fc2_int4": 3, "lowm": 4, "lora": 5, "mod_w4a16": 6}
-_SALT = {"fc2_mxfp4": 7919, "fc2_int4": 7919}
+         "fc2_int4": 3, "fc1_nvfp4": 3, "fc2_nvfp4": 3, "lowm": 4, "lora": 5, "mod_w4a16": 6}
+_SALT = {"fc2_mxfp4": 7919, "fc2_int4": 7919, "fc2_nvfp4": 7919}
 
 
 def layer_spec(name: str, **over) -> LayerSpec:
