@@ -30,10 +30,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of fused W4A4+low-rank linear, FLUX shapes; % of FP4 MFMA peak"
-PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 5000.0}          # MI355X dense FP4 / INT8 MFMA
+# MI355X dense MFMA peaks of the instruction each format runs on: FP4 (MXFP4),
+# INT8 (INT4 codes), fp16 (NVFP4-style codes, dequantized in registers)
+PEAK_TFLOPS = {"mxfp4": 10100.0, "int4": 5000.0, "nvfp4": 2500.0}
 PAIRS = {
     "mlp_mxfp4": ("fc1_mxfp4", "fc2_mxfp4"),
     "mlp_int4": ("fc1_int4", "fc2_int4"),
+    "mlp_nvfp4": ("fc1_nvfp4", "fc2_nvfp4"),
 }
 SINGLE = ("qkv", "lowm", "lora", "single")
 W4A16 = ("mod_w4a16",)

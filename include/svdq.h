@@ -19,6 +19,14 @@
  *   SVDQ_INT4_G64 : two's complement codes, one fp16 scale per 64;
  *                   s = fp16(fp32(amax / 7)) (clamped to 65504),
  *                   q = clamp(rint(fp32(x / s)), -8, 7), 0 when s == 0.
+ *   SVDQ_NVFP4    : the NVFP4-style format the Nunchaku in Diffusers page names
+ *                   for its Blackwell kernels: E2M1 codes, one E4M3 scale per 16,
+ *                   and a float32 tensor scale gs (R: gs = fp32(max|R| / 2688),
+ *                   computed at packing; X_hat: gs = 1).  Group scale byte =
+ *                   nearest E4M3 of fp32(fp32(amax / 6) / gs) (ties to even,
+ *                   saturating at 448), S = fp32(E4M3 * gs), codes = nearest E2M1
+ *                   of fp32(x / S) (ties to even, saturating at 6); signed zeros
+ *                   when S == 0.  Value = E2M1 * E4M3 * gs.
  * All float32 decision arithmetic is IEEE (correctly rounded divisions).
  *
  * Two launches per layer, as section 4.3 describes: svdq_quantize_act (smooth,
@@ -68,7 +76,8 @@ typedef enum {
 
 typedef enum {
   SVDQ_MXFP4 = 1,         /* E2M1 codes, E8M0 scale per 32 along K   */
-  SVDQ_INT4_G64 = 2       /* int4 codes, fp16 scale per 64 along K   */
+  SVDQ_INT4_G64 = 2,      /* int4 codes, fp16 scale per 64 along K   */
+  SVDQ_NVFP4 = 3          /* E2M1 codes, E4M3 scale per 16 along K, fp32 tensor scale */
 } svdq_format;
 
 /* Epilogue flags of svdq_gemm / svdq_linear. */
@@ -192,7 +201,8 @@ svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const ui
 /* Test access to the opaque layouts, in canonical form (device outputs, any may be NULL):
  *   codes   uint8 rows x K/2: two 4-bit codes per byte, element 2j in the low nibble
  *           of byte j (INT4 codes as 4-bit two's complement)
- *   scales  rows x K/32 uint8 E8M0 bytes (MXFP4) or rows x K/64 uint16 fp16 bits (INT4)
+ *   scales  rows x K/32 uint8 E8M0 bytes (MXFP4), rows x K/64 uint16 fp16 bits (INT4)
+ *           or rows x K/16 uint8 E4M3 bytes (NVFP4)
  *   weight: L1 (K x rank bf16), L2 (rank x N bf16), lambda (float32[K]), bias (bf16[N])
  *   act:    D (M x rank float32, the down projection as the GEMM epilogue consumes it) */
 svdq_status svdq_unpack_weight(const svdq_layer_desc* d, const void* w_packed, uint8_t* codes,

@@ -25,7 +25,7 @@ def pack(layer, L, torch, device, bias=True):
 
 def scales_np(t, fmt):
     a = t.cpu().numpy()
-    return a.view(np.uint8) if fmt == "mxfp4" else a.view(np.uint16)
+    return a.view(np.uint16) if fmt == "int4" else a.view(np.uint8)
 
 
 def bf16_to_np(t):

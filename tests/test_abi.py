@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 103
+    assert L.svdq_version() == 104
     for s in range(8):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -57,8 +57,11 @@ def test_size_queries(L):
     wb = L.svdq_weight_bytes(ctypes.byref(D()))
     assert wb >= 512 * 1024 // 2 + 512 * 1024 // 32 + 1024 * 32 * 2 + 512 * 32 * 2 + 1024 * 8 + 512 * 2
     assert wb % 256 == 0
-    # the two formats use the same bytes (E8M0 per 32 vs fp16 per 64)
+    # MXFP4 and INT4 use the same bytes (E8M0 per 32 vs fp16 per 64); NVFP4 one
+    # more scale byte per 32 (E4M3 per 16), rows padded to 512 here
     assert L.svdq_weight_bytes(ctypes.byref(D(fmt=2))) == wb
+    assert L.svdq_weight_bytes(ctypes.byref(D(fmt=3))) == wb + 512 * 1024 // 32
+    assert L.svdq_act_bytes(ctypes.byref(D(fmt=3)), 4608) > L.svdq_act_bytes(ctypes.byref(D()), 4608)
     a1 = L.svdq_act_bytes(ctypes.byref(D()), 1)
     a2 = L.svdq_act_bytes(ctypes.byref(D()), 4608)
     assert 0 < a1 < a2 and a2 >= 4608 * 1024 // 2 + 4608 * 1024 // 32 + 4608 * 32 * 4

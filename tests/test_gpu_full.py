@@ -16,7 +16,7 @@ from _gpu_helpers import (assert_codes_equal, assert_scales_equal, bf16_to_np, c
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["single", "qkv", "fc1_mxfp4", "fc2_mxfp4", "fc1_int4", "fc2_int4", "lowm", "lora"]
+FULL = ["single", "qkv", "fc1_mxfp4", "fc2_mxfp4", "fc1_int4", "fc2_int4", "fc1_nvfp4", "fc2_nvfp4", "lowm", "lora"]
 
 
 @pytest.fixture(scope="module")
@@ -59,7 +59,8 @@ def test_full_size_sampled(torch_dev, name):
     cX, sX = Q.quantize(xhat, spec.fmt)
     assert_codes_equal(ua["codes"][rows].cpu().numpy(), cX, "activation codes (sampled rows)")
     assert_scales_equal(scales_np(ua["scales"][rows], spec.fmt), sX, "activation scales (sampled rows)")
-    cR, sR = Q.quantize(L["R"][cols], spec.fmt)
+    gsR = Q.nvfp4_global_scale(L["R"]) if spec.fmt == "nvfp4" else 1.0   # of the whole residual
+    cR, sR = Q.quantize(L["R"][cols], spec.fmt, gsR)
     assert_codes_equal(uw["codes"][cols].cpu().numpy(), cR, "weight codes (sampled columns)")
     assert_scales_equal(scales_np(uw["scales"][cols], spec.fmt), sR, "weight scales (sampled columns)")
 
@@ -70,7 +71,7 @@ def test_full_size_sampled(torch_dev, name):
     check_bf16_output(bf16_to_np(Yb)[sel], Y_o, f"{name} bf16 output")
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4", "nvfp4"])
 def test_mlp_pair_chain(torch_dev, fmt):
     """fc1 (GELU fused) -> bf16 H -> fc2 on the GPU against the same chain in the
     oracle (each side uses its own H), at a reduced size with several tiles."""

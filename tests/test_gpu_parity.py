@@ -42,6 +42,9 @@ MEDIUM = [
     ("lora", "mxfp4", 513, 2048, 784, 48, 5),
     ("lowm", "mxfp4", 64, 512, 16, 256, 6),
     ("lowm", "int4", 130, 512, 48, 128, 7),
+    ("qkv", "nvfp4", 300, 1024, 512, 16, 8),
+    ("lowm", "nvfp4", 1, 512, 48, 0, 9),
+    ("lora", "nvfp4", 513, 2048, 784, 48, 10),
 ]
 
 
@@ -157,7 +160,7 @@ def test_gelu_epilogue_pointwise(torch_dev):
     assert np.all(err <= 1e-6 * np.maximum(1.0, np.abs(b))), f"max GELU error {err.max():.3e}"
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4", "nvfp4"])
 def test_edge_values_bit_exact(torch_dev, fmt):
     """Zero rows, signed zeros, subnormal inputs after smoothing, huge values:
     codes and scales still match the oracle bit for bit."""
@@ -179,7 +182,7 @@ def test_edge_values_bit_exact(torch_dev, fmt):
     assert np.all(np.isfinite(Y.cpu().numpy()))
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4", "nvfp4"])
 @pytest.mark.parametrize("lam_edge", ["inside", "outside"])
 def test_division_range_edges_bit_exact(torch_dev, fmt, lam_edge):
     """Smoothing quotients at the edges of the range the activation kernel's

@@ -11,10 +11,11 @@ from __future__ import annotations
 import ctypes
 from dataclasses import dataclass
 
-from ._lib import (EPI_BIAS, EPI_GELU, EPI_LOWRANK, EPI_OUT_F32, INT4_G64, MXFP4, LIB_PATH,  # noqa: F401
+from ._lib import (EPI_BIAS, EPI_GELU, EPI_LOWRANK, EPI_OUT_F32, INT4_G64, MXFP4, NVFP4, LIB_PATH,  # noqa: F401
                    LayerDesc, SvdqError, check, lib)
 
-FORMATS = {"mxfp4": MXFP4, "int4": INT4_G64}
+FORMATS = {"mxfp4": MXFP4, "int4": INT4_G64, "nvfp4": NVFP4}
+GROUPS = {"mxfp4": 32, "int4": 64, "nvfp4": 16}
 
 
 @dataclass(frozen=True)
@@ -31,7 +32,7 @@ class Layer:
 
     @property
     def group(self) -> int:
-        return 32 if self.fmt == "mxfp4" else 64
+        return GROUPS[self.fmt]
 
 
 def _torch():
@@ -165,6 +166,12 @@ def linear(layer: Layer, w_packed, X, epi: int, out=None, workspace=None, stream
     return out
 
 
+def _scales_out(torch, layer: Layer, rows: int, dev):
+    """Canonical scales: one byte per group (E8M0 for MXFP4, E4M3 for NVFP4) or fp16 bits (INT4)."""
+    dt = torch.int16 if layer.fmt == "int4" else torch.uint8
+    return torch.empty((rows, layer.K // layer.group), dtype=dt, device=dev)
+
+
 def unpack_weight(layer: Layer, w_packed, stream=None) -> dict:
     """Canonical codes (N x K/2), scales, L1, L2, lambda and bias of a packed weight."""
     torch = _torch()
@@ -172,10 +179,7 @@ def unpack_weight(layer: Layer, w_packed, stream=None) -> dict:
     dev = w_packed.device
     K, N, r = layer.K, layer.N, layer.rank
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    if layer.fmt == "mxfp4":
-        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
-    else:
-        scales = torch.empty((N, K // 64), dtype=torch.int16, device=dev)
+    scales = _scales_out(torch, layer, N, dev)
     L1 = torch.empty((K, r), dtype=torch.int16, device=dev)
     L2 = torch.empty((r, N), dtype=torch.int16, device=dev)
     lam = torch.empty(K, dtype=torch.float32, device=dev)
@@ -193,10 +197,7 @@ def unpack_act(layer: Layer, a_packed, M: int, stream=None) -> dict:
     dev = a_packed.device
     K, r = layer.K, layer.rank
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    if layer.fmt == "mxfp4":
-        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
-    else:
-        scales = torch.empty((M, K // 64), dtype=torch.int16, device=dev)
+    scales = _scales_out(torch, layer, M, dev)
     D = torch.empty((M, r), dtype=torch.float32, device=dev)
     st = lib().svdq_unpack_act(p, _ptr(a_packed), M, _ptr(codes), _ptr(scales), _ptr(D if r else None),
                                _stream(stream))

@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvdq.so"
 
 MXFP4 = 1
 INT4_G64 = 2
+NVFP4 = 3
 EPI_LOWRANK = 1
 EPI_BIAS = 2
 EPI_GELU = 4

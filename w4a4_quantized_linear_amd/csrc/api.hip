@@ -10,7 +10,7 @@
 
 namespace svdq {
 hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
-                                  uint8_t* scales, int64_t rows_pad, hipStream_t s);
+                                  uint8_t* scales, int64_t rows_pad, uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t ld, int K, const float* lam,
                                const float* rlam, const float* rlo, const void* L1f, uint8_t* codes, uint8_t* scales,
                                int64_t rows_pad,
@@ -56,7 +56,7 @@ svdq_status check_shape(const svdq_layer_desc* d) {
 }
 
 svdq_status check_fmt(const svdq_layer_desc* d) {
-  return (d->fmt == SVDQ_MXFP4 || d->fmt == SVDQ_INT4_G64) ? SVDQ_OK : SVDQ_ERR_FORMAT;
+  return (d->fmt == SVDQ_MXFP4 || d->fmt == SVDQ_INT4_G64 || d->fmt == SVDQ_NVFP4) ? SVDQ_OK : SVDQ_ERR_FORMAT;
 }
 
 // Architecture check, cached per device: 0 unknown, 1 gfx950, 2 other.
@@ -110,7 +110,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 103; }
+int svdq_version(void) { return 104; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -134,12 +134,12 @@ void svdq_test_force_device_error(int on) { g_force_device_fail.store(on ? 1 : 0
 
 size_t svdq_weight_bytes(const svdq_layer_desc* d) {
   if (!d || check_shape(d) != SVDQ_OK || check_fmt(d) != SVDQ_OK) return 0;
-  return weight_layout(d->K, d->N, d->rank).total;
+  return weight_layout(d->fmt, d->K, d->N, d->rank).total;
 }
 
 size_t svdq_act_bytes(const svdq_layer_desc* d, int64_t M) {
   if (!d || check_shape(d) != SVDQ_OK || check_fmt(d) != SVDQ_OK || M < 0 || M > kMaxRows) return 0;
-  return act_layout(d->K, d->rank, M).total;
+  return act_layout(d->fmt, d->K, d->rank, M).total;
 }
 
 svdq_status svdq_pack_weight(const svdq_layer_desc* d, const float* R, const uint16_t* L1, const uint16_t* L2,
@@ -153,10 +153,11 @@ svdq_status svdq_pack_weight(const svdq_layer_desc* d, const float* R, const uin
       (L2 && !aligned(L2, 2)) || (bias && !aligned(bias, 2)))
     return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
   uint8_t* blob = static_cast<uint8_t*>(w_packed);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_quantize_weight(d->fmt, R, d->N, d->K, d->K, blob + wl.codes, blob + wl.scales, wl.N_pad, st);
+  hipError_t e = launch_quantize_weight(d->fmt, R, d->N, d->K, d->K, blob + wl.codes, blob + wl.scales, wl.N_pad,
+                                        reinterpret_cast<uint32_t*>(blob + wl.amax), st);
   if (e != hipSuccess) return SVDQ_ERR_LAUNCH;
   return launched(launch_pack_aux(L1, L2, lambda, bias, d->K, d->N, d->rank, wl, blob, st));
 }
@@ -167,8 +168,8 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* d, const void* w_packed, co
   if (s != SVDQ_OK) return s;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
-  const ActLayout al = act_layout(d->K, d->rank, M);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
   uint8_t* ws = static_cast<uint8_t*>(a_packed);
   return launched(launch_quantize_act(d->fmt, X, M, ldx, d->K, reinterpret_cast<const float*>(blob + wl.lam),
@@ -186,8 +187,8 @@ svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void
   if (s != SVDQ_OK) return s;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
-  const ActLayout al = act_layout(d->K, d->rank, M);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
   return launched(launch_gemm(d->fmt, static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                               al, d->K, d->N, M, Y, ldy, epi, static_cast<hipStream_t>(stream)));
 }
@@ -206,10 +207,10 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
     return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
-  const ActLayout al = act_layout(d->K, d->rank, M);
-  const WeightLayout nwl = weight_layout(dn->K, dn->N, dn->rank);
-  const ActLayout nal = act_layout(dn->K, dn->rank, M);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
+  const WeightLayout nwl = weight_layout(dn->fmt, dn->K, dn->N, dn->rank);
+  const ActLayout nal = act_layout(dn->fmt, dn->K, dn->rank, M);
   return launched(launch_gemm_quant(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                     al, d->K, d->N, M, epi, static_cast<const uint8_t*>(wn_packed), nwl,
                                     static_cast<uint8_t*>(an_packed), nal, static_cast<hipStream_t>(stream)));
@@ -232,8 +233,8 @@ svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const 
     return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
-  const ActLayout al = act_layout(d->K, d->rank, M);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
   return launched(launch_gemm_qkv(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                   al, d->K, d->N, M, Y, ldy, epi, norm_q, norm_k, eps, rope_cos, rope_sin,
                                   static_cast<hipStream_t>(stream)));
@@ -252,7 +253,7 @@ svdq_status svdq_gemm_w4a16(const svdq_layer_desc* d, const void* w_packed, cons
     return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
   return launched(launch_gemm_w4a16(static_cast<const uint8_t*>(w_packed), wl, d->K, d->N, X, ldx, M, Y, ldy, epi,
                                     static_cast<hipStream_t>(stream)));
 }
@@ -262,7 +263,7 @@ svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const ui
   svdq_status s = check_act_args(d, w_packed, X, M, ldx, workspace);
   if (s != SVDQ_OK) return s;
   if ((s = check_gemm_args(d, w_packed, workspace, M, Y, ldy, epi)) != SVDQ_OK) return s;
-  if (ws_bytes < act_layout(d->K, d->rank, M).total) return SVDQ_ERR_WORKSPACE;
+  if (ws_bytes < act_layout(d->fmt, d->K, d->rank, M).total) return SVDQ_ERR_WORKSPACE;
   if ((s = device_check()) != SVDQ_OK) return s;
   if (M == 0) return SVDQ_OK;
   if ((s = svdq_quantize_act(d, w_packed, X, M, ldx, workspace, stream)) != SVDQ_OK) return s;
@@ -277,7 +278,7 @@ svdq_status svdq_unpack_weight(const svdq_layer_desc* d, const void* w_packed, u
   if ((s = check_fmt(d)) != SVDQ_OK) return s;
   if (!aligned(w_packed, 256)) return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
-  const WeightLayout wl = weight_layout(d->K, d->N, d->rank);
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
   return launched(launch_unpack_weight(d->fmt, d->K, d->N, d->rank, wl, static_cast<const uint8_t*>(w_packed), codes,
                                        scales, L1, L2, lambda, bias, static_cast<hipStream_t>(stream)));
 }
@@ -291,7 +292,7 @@ svdq_status svdq_unpack_act(const svdq_layer_desc* d, const void* a_packed, int6
   if ((s = check_fmt(d)) != SVDQ_OK) return s;
   if (!aligned(a_packed, 256)) return SVDQ_ERR_ALIGN;
   if ((s = device_check()) != SVDQ_OK) return s;
-  const ActLayout al = act_layout(d->K, d->rank, M);
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
   return launched(launch_unpack_act(d->fmt, d->K, d->rank, M, al, static_cast<const uint8_t*>(a_packed), codes, scales,
                                     D, static_cast<hipStream_t>(stream)));
 }

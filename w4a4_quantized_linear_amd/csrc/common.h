@@ -77,6 +77,11 @@ __device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL, int(sa), SEL, int(sb));
 }
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_f16(const uint4& a, const uint4& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ v4f mfma_bf16(const uint4& a, const uint4& b, v4f c) {
   v8s as = {short(a.x), short(a.x >> 16), short(a.y), short(a.y >> 16),
             short(a.z), short(a.z >> 16), short(a.w), short(a.w >> 16)};
@@ -105,6 +110,34 @@ __device__ __forceinline__ void unpack_i4x8(uint32_t d, int& first, int& second)
 __device__ __forceinline__ void unpack_bf8(const uint4& r, float (&a)[8]) {
   a[0] = bf_lo(r.x); a[1] = bf_hi(r.x); a[2] = bf_lo(r.y); a[3] = bf_hi(r.y);
   a[4] = bf_lo(r.z); a[5] = bf_hi(r.z); a[6] = bf_lo(r.w); a[7] = bf_hi(r.w);
+}
+
+// max over the lanes l and l ^ 16 (the 2 lanes that hold a 16-element half of a row's 32-block)
+__device__ __forceinline__ float rowpair_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+}
+
+// Nearest E4M3 byte of a non-negative u (ties to even), saturating at 448 (also
+// for +inf).  Below 2^-6 the format's step is 2^-9, so the byte is rint(u 2^9)
+// (8 is the smallest normal, whose byte is 8); above, the fp32 mantissa is
+// rounded to 3 bits and a carry runs into the exponent field.
+__device__ __forceinline__ uint32_t e4m3_rne(float u) {
+  if (!(u < 448.0f)) return 0x7Eu;
+  const uint32_t b = __float_as_uint(u);
+  const int E = int(b >> 23) - 127;
+  if (E < -6) return uint32_t(__builtin_rintf(u * 512.0f));
+  const uint32_t m = b & 0x7FFFFFu;
+  const uint32_t keep = m >> 20, rem = m & 0xFFFFFu;
+  const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
+  return (uint32_t(E + 7) << 3) + keep + up;
+}
+
+// fp32 value of a non-negative E4M3 byte (sign bit clear, not the NaN code).
+__device__ __forceinline__ float e4m3_value(uint32_t s) {
+  const uint32_t ex = (s >> 3) & 15u, mn = s & 7u;
+  return ex == 0 ? float(mn) * 0.001953125f : __uint_as_float(((ex + 120u) << 23) | (mn << 20));
 }
 
 // max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the 4 lanes that hold one row's group)

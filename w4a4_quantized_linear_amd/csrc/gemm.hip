@@ -28,7 +28,7 @@ namespace svdq {
 struct GemmArgs {
   const uint8_t* wblob;
   const uint8_t* act;
-  size_t w_codes, w_scales, w_L2, w_bias;
+  size_t w_codes, w_scales, w_L2, w_bias, w_amax;
   size_t a_codes, a_scales, a_D;
   int64_t N_pad, M_pad, M, ldy;
   int K, N, r_pad;
@@ -741,6 +741,137 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
 }
 
+// ------------------------------------------------------------------ NVFP4
+//
+// The NVFP4-style format (E2M1 codes, an E4M3 scale per 16, a float32 tensor
+// scale) has no matrix instruction on gfx950: the scaled FP4 MFMA takes one
+// power-of-two scale per 32.  Both operands are therefore dequantized in
+// registers to fp16 and multiplied on the fp16 MFMA (16 x 16 x 32): the gfx950
+// FP4 convert applies the power of two 2^floor(log2 S) of the group scale S,
+// then a packed fp16 multiply applies S's mantissa (1.xxx).  The value
+// code * S has at most 6 significant bits and lies in [2^-10, 2880], so it is
+// exact in fp16, every product is exact in fp32, and the fp32 sums round like
+// any other accumulation.  The tensor scale multiplies the sum before the
+// epilogue.  Tiles, prefetch and epilogue follow the INT4 kernel.
+
+// 8 E2M1 codes of one dword (code e in byte e / 2, low nibble for even e) -> 4
+// dwords of fp16 pairs code * S, in code order; sf = S as fp32, m2 = S's
+// mantissa as fp16 in both halves.
+__device__ __forceinline__ uint4 nv_dequant8(uint32_t d, float sf, uint32_t m2) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 mm = __builtin_bit_cast(h2, m2);
+  const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sf, 0) * mm;
+  const h2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sf, 1) * mm;
+  const h2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sf, 2) * mm;
+  const h2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, sf, 3) * mm;
+  return make_uint4(__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
+                    __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3));
+}
+
+// The group scale S of half h of a lane's 32-element block (byte h of the
+// lane's two E4M3 bytes) as fp32, and its mantissa 1.xxx as fp16 in both halves
+// of a dword (1.0 when S == 0).
+struct NvScale { float sf; uint32_t m2; };
+__device__ __forceinline__ NvScale nv_scale(uint32_t s2, int h) {
+  const float sf = e4m3_value((s2 >> (8 * h)) & 0xFFu);
+  const uint32_t m16 = 0x3C00u | ((__float_as_uint(sf) >> 13) & 0x3FFu);
+  return NvScale{sf, m16 | (m16 << 16)};
+}
+
+template <int WN, int WM>
+struct Nv4Stage {
+  uint4 cw[WN], cx[WM];       // codes of the weight and activation fragments
+  uint32_t sw[WN], sx[WM];    // the lane's two E4M3 group scales per fragment
+};
+
+template <int WN, int WM, bool OUT_F32, bool GELU>
+__global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
+  const int tiles_m = int(g.M_pad / BM);
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int64_t n0 = int64_t(tn) * BN + (w & 1) * (WN * 16);
+  const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
+  const int KS = g.K / kKStep;
+
+  const uint4* Wc = reinterpret_cast<const uint4*>(g.wblob + g.w_codes) + (n0 / 16) * KS * 64 + lane;
+  const uint4* Ac = reinterpret_cast<const uint4*>(g.act + g.a_codes) + (m0 / 16) * KS * 64 + lane;
+  // scales: per 16-row tile and step, lane L's two bytes at 2 L
+  const uint16_t* Wsc = reinterpret_cast<const uint16_t*>(g.wblob + g.w_scales) + (n0 / 16) * KS * 64 + lane;
+  const uint16_t* Asc = reinterpret_cast<const uint16_t*>(g.act + g.a_scales) + (m0 / 16) * KS * 64 + lane;
+
+  auto load = [&](int ks, Nv4Stage<WN, WM>& st) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      st.cw[i] = Wc[(size_t(i) * KS + ks) * 64];
+      st.sw[i] = Wsc[(size_t(i) * KS + ks) * 64];
+    }
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      st.cx[j] = Ac[(size_t(j) * KS + ks) * 64];
+      st.sx[j] = Asc[(size_t(j) * KS + ks) * 64];
+    }
+  };
+
+  v4f acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // MFMA chunk u of a step takes elements 8u .. 8u + 7 of every lane's
+  // 32-element block (dword u of its codes, group half u / 2), on both operands
+  auto compute = [&](const Nv4Stage<WN, WM>& st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      NvScale sa[WN], sb[WM];
+#pragma unroll
+      for (int i = 0; i < WN; ++i) sa[i] = nv_scale(st.sw[i], h);
+#pragma unroll
+      for (int j = 0; j < WM; ++j) sb[j] = nv_scale(st.sx[j], h);
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * h + uu;
+        uint4 a[WN], b[WM];
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          const uint32_t q = u == 0 ? st.cx[j].x : u == 1 ? st.cx[j].y : u == 2 ? st.cx[j].z : st.cx[j].w;
+          b[j] = nv_dequant8(q, sb[j].sf, sb[j].m2);
+        }
+#pragma unroll
+        for (int i = 0; i < WN; ++i) {
+          const uint32_t q = u == 0 ? st.cw[i].x : u == 1 ? st.cw[i].y : u == 2 ? st.cw[i].z : st.cw[i].w;
+          a[i] = nv_dequant8(q, sa[i].sf, sa[i].m2);
+        }
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+#pragma unroll
+          for (int j = 0; j < WM; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+      }
+    }
+  };
+
+  // two register sets, one computing while the other fills (KS is a multiple
+  // of 4; the final load repeats the last step, in bounds and unused)
+  Nv4Stage<WN, WM> s0, s1;
+  load(0, s0);
+  for (int ks = 0; ks < KS; ks += 2) {
+    load(ks + 1, s1);
+    compute(s0);
+    load(ks + 2 < KS ? ks + 2 : KS - 1, s0);
+    compute(s1);
+  }
+  // the weight tensor scale gs = fp32(max|R| / 2688); the activations' is 1
+  const float gs = __uint_as_float(*reinterpret_cast<const uint32_t*>(g.wblob + g.w_amax)) / kNvfp4GlobalDiv;
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = acc[i][j] * gs;
+  __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
+  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+}
+
 // ------------------------------------------------------------------ W4A16
 //
 // The second kernel family of the Nunchaku in Diffusers page (section
@@ -992,7 +1123,7 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
   GemmArgs g{};
   g.wblob = wblob;
   g.act = act;
-  g.w_codes = wl.codes; g.w_scales = wl.scales; g.w_L2 = wl.L2; g.w_bias = wl.bias;
+  g.w_codes = wl.codes; g.w_scales = wl.scales; g.w_L2 = wl.L2; g.w_bias = wl.bias; g.w_amax = wl.amax;
   g.a_codes = al.codes; g.a_scales = al.scales; g.a_D = al.D;
   g.N_pad = wl.N_pad; g.M_pad = al.M_pad; g.M = M; g.ldy = ldy;
   g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
@@ -1032,6 +1163,9 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
     }
+  } else if (fmt == kFmtNVFP4) {
+    const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
+    SVDQ_LAUNCH(gemm_nvfp4_kernel, 4, 4, 256, nb);
   } else {
     const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
     SVDQ_LAUNCH(gemm_int4_kernel, 4, 4, 256, nb);

@@ -18,6 +18,11 @@
 //   order, which is what both the int8 expansion and the bf16 conversion of the
 //   W4A16 kernel want.  Scales: per 128-K step and row, two fp16 (groups 0 and
 //   1) in 4 bytes, rows contiguous.
+// NVFP4-style (E2M1 codes, an E4M3 scale per 16): the codes use the MXFP4
+//   fragment layout (lane L: row L%16, 32-element block L/16, 16 B).  Scales:
+//   per 16-row tile and 128-K step, lane L's two E4M3 bytes (its block's halves
+//   0 and 1) at 2 L, 128 B per tile-step.  The weight blob also holds the
+//   residual's max |R| (fp32 bits), from which the tensor scale is derived.
 // bf16 MFMA (v_mfma_f32_16x16x32_bf16) fragments for the low-rank branch: lane
 //   L holds row/column L%16 and 8 consecutive K (rank) elements at (L/16)*8.
 //
@@ -35,6 +40,11 @@ constexpr int kKSuper = 512;       // K per scale superfragment; K must be a mul
 constexpr int kRankAlign = 32;     // rank padded to the bf16 MFMA K
 constexpr int kFmtMXFP4 = 1;
 constexpr int kFmtINT4 = 2;
+constexpr int kFmtNVFP4 = 3;
+constexpr float kNvfp4GlobalDiv = 2688.0f;   // E2M1 max 6 times E4M3 max 448
+
+// Scale bytes per row: K/32 (E8M0 per 32, or fp16 per 64), K/16 for NVFP4 (E4M3 per 16).
+__host__ __device__ inline size_t scale_row_bytes(int fmt, int K) { return fmt == kFmtNVFP4 ? K / 16 : K / 32; }
 constexpr uint32_t kLamRangeBit = 1;   // weight flags: a lambda outside [2^-32, 2^32]
 constexpr uint32_t kDivSlowBit = 2;    // weight flags: the two-operation division is not exact for some lambda
 
@@ -43,7 +53,7 @@ __host__ __device__ inline size_t align256(size_t a) { return (a + 255) & ~size_
 
 struct WeightLayout {
   int64_t N_pad, r_pad;
-  size_t codes, scales, L1, L2, lam, rlam, rlo, bias, flags, total;
+  size_t codes, scales, L1, L2, lam, rlam, rlo, bias, flags, amax, total;
 };
 
 struct ActLayout {
@@ -52,18 +62,18 @@ struct ActLayout {
   size_t codes, scales, D, part, total;
 };
 
-// Codes: N_pad x K/2 bytes.  Scales: N_pad x K/32 bytes (E8M0 per 32, or fp16 per 64).
+// Codes: N_pad x K/2 bytes.  Scales: N_pad x scale_row_bytes(fmt, K) bytes.
 // L1: K x r_pad bf16 (B fragments of the down projection).  L2: N_pad x r_pad bf16
 // (A fragments of the up projection).  lambda, r = RN(1/lambda) and the correction
 // rl = RN((1 - r lambda) r): fp32[K] each.  bias: bf16[N_pad].  flags: uint32
-// (kLamRangeBit, kDivSlowBit).
-__host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
+// (kLamRangeBit, kDivSlowBit).  amax: the NVFP4 residual's max |R| as fp32 bits.
+__host__ __device__ inline WeightLayout weight_layout(int fmt, int K, int N, int rank) {
   WeightLayout w;
   w.N_pad = round_up(N, kTileRows);
   w.r_pad = round_up(rank, kRankAlign);
   size_t o = 0;
   w.codes = o;  o = align256(o + size_t(w.N_pad) * K / 2);
-  w.scales = o; o = align256(o + size_t(w.N_pad) * K / 32);
+  w.scales = o; o = align256(o + size_t(w.N_pad) * scale_row_bytes(fmt, K));
   w.L1 = o;     o = align256(o + size_t(K) * w.r_pad * 2);
   w.L2 = o;     o = align256(o + size_t(w.N_pad) * w.r_pad * 2);
   w.lam = o;    o = align256(o + size_t(K) * 4);
@@ -71,6 +81,7 @@ __host__ __device__ inline WeightLayout weight_layout(int K, int N, int rank) {
   w.rlo = o;    o = align256(o + size_t(K) * 4);
   w.bias = o;   o = align256(o + size_t(w.N_pad) * 2);
   w.flags = o;  o = align256(o + 4);
+  w.amax = o;   o = align256(o + 4);
   w.total = o;
   return w;
 }
@@ -99,19 +110,19 @@ __host__ __device__ inline void act_split(int K, int r_pad, int64_t M_pad, int* 
   *splits = K / kr;
 }
 
-// Codes: M_pad x K/2.  Scales: M_pad x K/32 bytes.  D: M_pad x r_pad x {hi, lo} bf16.
+// Codes: M_pad x K/2.  Scales: M_pad x scale_row_bytes(fmt, K).  D: M_pad x r_pad x {hi, lo} bf16.
 // part: fp32 partial down projections, P x M_pad x r_pad, for the larger of the two
 // producers: the activation kernel's K splits (when it splits K), and the GEMM of a
 // previous layer that quantizes its output for this layer (one partial per 256
 // columns of that output, K / 256 of them).
-__host__ __device__ inline ActLayout act_layout(int K, int rank, int64_t M) {
+__host__ __device__ inline ActLayout act_layout(int fmt, int K, int rank, int64_t M) {
   ActLayout a;
   a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
   a.r_pad = round_up(rank, kRankAlign);
   act_split(K, int(a.r_pad), a.M_pad, &a.kr, &a.splits);
   size_t o = 0;
   a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
-  a.scales = o; o = align256(o + size_t(a.M_pad) * K / 32);
+  a.scales = o; o = align256(o + size_t(a.M_pad) * scale_row_bytes(fmt, K));
   a.D = o;      o = align256(o + size_t(a.M_pad) * a.r_pad * 4);
   const int nparts = (a.splits > 1 && a.splits > K / kTileRows) ? a.splits : K / kTileRows;
   a.part = o;   o = align256(o + size_t(nparts) * a.M_pad * a.r_pad * 4);
@@ -130,7 +141,7 @@ __host__ __device__ inline size_t code_byte(int fmt, int64_t row, int k, int K, 
   const int r = int(row % 16);
   const int ks = k / kKStep;
   const int kk = k % kKStep;
-  if (fmt == kFmtMXFP4) {
+  if (fmt != kFmtINT4) {                         // MXFP4 and NVFP4
     const int blk = kk / 32, t = kk % 32;
     *hi = t & 1;
     return code_chunk(rt, ks, K, blk * 16 + r) + t / 2;
@@ -148,6 +159,13 @@ __host__ __device__ inline size_t mx_scale_byte(int64_t row, int kb, int K) {
   const int ks = kb / 4, blk = kb % 4;          // 128-K step and block within it
   const int sup = ks / 4, j = ks % 4;           // superfragment and byte within the dword
   return ((size_t(rt) * (K / kKSuper) + sup) * 64 + (blk * 16 + r)) * 4 + j;
+}
+// NVFP4: byte offset of the E4M3 scale of (row, 16-group index kg) (kg = k / 16).
+__host__ __device__ inline size_t nv_scale_byte(int64_t row, int kg, int K) {
+  const int64_t rt = row / 16;
+  const int r = int(row % 16);
+  const int ks = kg / 8, blk = (kg / 2) % 4, half = kg % 2;
+  return ((size_t(rt) * (K / kKStep) + ks) * 64 + (blk * 16 + r)) * 2 + half;
 }
 // INT4: byte offset of the fp16 scale of (row, 64-group index g) with rows padded to rows_pad.
 __host__ __device__ inline size_t i4_scale_byte(int64_t row, int g, int64_t rows_pad) {

@@ -20,7 +20,8 @@ namespace svdq {
 template <int FMT>
 __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __restrict__ src, int64_t rows,
                                                               int64_t ld, int K, uint8_t* __restrict__ codes,
-                                                              uint8_t* __restrict__ scales, int64_t rows_pad) {
+                                                              uint8_t* __restrict__ scales, int64_t rows_pad,
+                                                              const uint32_t* __restrict__ amax_bits) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -29,6 +30,8 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
   const int64_t m = rt * 16 + row;
   const bool valid = m < rows;
   const int nsuper = K / kKSuper;
+  // NVFP4: the tensor scale gs = fp32(max|R| / 2688)
+  const float gs = FMT == kFmtNVFP4 ? __uint_as_float(*amax_bits) / kNvfp4GlobalDiv : 1.0f;
 
   for (int kc = w; kc < nsuper; kc += nw) {
     uint32_t sdw = 0;  // MXFP4: this lane's scale dword of the superfragment
@@ -67,6 +70,34 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
           const int ks = kc * 4 + jb / 4;
           *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (jb & 3) * 16 + row) + c * 4) = cw;
           if ((jb & 3) == c) sdw |= sb << (8 * (jb >> 2));
+        }
+      } else if (FMT == kFmtNVFP4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int jb = 2 * p + h;  // 32-block within the superchunk
+          // this lane's 8 elements are half c / 2 of the 32-block: a 16-group
+          // shared with lane ^ 16
+          float amax = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+          amax = rowpair_max(amax);
+          const float a6 = amax / 6.0f;
+          const uint32_t sb = e4m3_rne(gs != 0.0f ? a6 / gs : 0.0f);
+          const float S = e4m3_value(sb) * gs;
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = S != 0.0f ? x[8 * h + e] / S : x[8 * h + e] * 0.0f;
+          uint32_t cw = 0;
+          cw = cvt_fp4x2<0>(cw, t[0], t[1]);
+          cw = cvt_fp4x2<1>(cw, t[2], t[3]);
+          cw = cvt_fp4x2<2>(cw, t[4], t[5]);
+          cw = cvt_fp4x2<3>(cw, t[6], t[7]);
+          const int ks = kc * 4 + jb / 4;
+          *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (jb & 3) * 16 + row) + c * 4) = cw;
+          if ((c & 1) == 0) {
+            const int kg = (kc * kKSuper + jb * 32) / 16 + c / 2;
+            scales[nv_scale_byte(m, kg, K)] = uint8_t(sb);
+          }
         }
       } else {
         float amax = 0.f;
@@ -159,7 +190,10 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + row0 * ld + k_beg, uint32_t((16 * ld) * 2));
   const uint32_t xoff = uint32_t((my_row - row0) * ld * 2 + c * 16);
   const __amdgpu_buffer_rsrc_t rC = make_rsrc(codes + size_t(rt) * KS * 1024, uint32_t(KS) * 1024);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(scales + size_t(rt) * nsuper * 256, uint32_t(nsuper) * 256);
+  // scales of the tile: MXFP4 nsuper superfragments of 256 B; NVFP4 KS steps of 128 B
+  const __amdgpu_buffer_rsrc_t rS =
+      FMT == kFmtNVFP4 ? make_rsrc(scales + size_t(rt) * KS * 128, uint32_t(KS) * 128)
+                       : make_rsrc(scales + size_t(rt) * nsuper * 256, uint32_t(nsuper) * 256);
   auto load_x = [&](int p, uint4& lo, uint4& hi) {
     const int q = p < nsteps ? p : nsteps - 1;   // past the end: an in-bounds load that is never used
     lo = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff, uint32_t(q) * 128, 0));
@@ -256,6 +290,44 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
         if (c == (kb & 3))
           __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sb), rS, uint32_t(lane * 4), uint32_t((kb / 16) * 256 + ks % 4),
                                                0);
+      }
+    } else if (FMT == kFmtNVFP4) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = kb0 + h;
+        // the lane's 8 elements are half c / 2 of the 32-block, a 16-group shared with lane ^ 16;
+        // the activations' tensor scale is 1, so the group scale is E4M3(amax / 6)
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+        amax = rowpair_max(amax);
+        const uint32_t sb = e4m3_rne(amax / 6.0f);
+        const float S = e4m3_value(sb);
+        const float rs = 1.0f / S;
+        float t[8];
+        if (__builtin_expect(fast, 1)) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = div_refined(x[8 * h + e], S, rs);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = x[8 * h + e] / S;
+        }
+        // a zero scale (the whole group rounds it to 0): signed zeros
+        if (S == 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = x[8 * h + e] * 0.0f;
+        }
+        uint32_t cw = 0;
+        cw = cvt_fp4x2<0>(cw, t[0], t[1]);
+        cw = cvt_fp4x2<1>(cw, t[2], t[3]);
+        cw = cvt_fp4x2<2>(cw, t[4], t[5]);
+        cw = cvt_fp4x2<3>(cw, t[6], t[7]);
+        __builtin_amdgcn_raw_buffer_store_b32(cw, rC, uint32_t(row * 16 + c * 4),
+                                              uint32_t(ks * 1024 + (kb & 3) * 256), 0);
+        // scale byte of (row, 16-group): GEMM lane (kb & 3) * 16 + row, half c / 2
+        if ((c & 1) == 0)
+          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(sb), rS, uint32_t(((kb & 3) * 16 + row) * 2 + c / 2),
+                                               uint32_t(ks * 128), 0);
       }
     } else {
       float amax = 0.f;
@@ -484,6 +556,27 @@ __global__ void __launch_bounds__(1024) check_lambda_kernel(const float* __restr
   if (threadIdx.x == 0) *flags = red[0];
 }
 
+// ---- NVFP4 tensor maximum (load time) ----
+
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+// max |R| over rows x K (row stride ld) into *out as fp32 bits: non-negative
+// floats order like their bit patterns, so an unsigned atomic max suffices.
+__global__ void __launch_bounds__(256) abs_max_kernel(const float* __restrict__ src, int64_t rows, int64_t ld, int K,
+                                                      uint32_t* __restrict__ out) {
+  const int64_t total = rows * (K / 4);
+  float m = 0.f;
+  for (int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; d < total; d += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = d / (K / 4);
+    const int j = int(d % (K / 4));
+    const float4 v = *reinterpret_cast<const float4*>(src + r * ld + 4 * j);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+}
+
 // ---- test-only unpackers to the canonical layout ----
 
 __global__ void unpack_codes_kernel(int fmt, const uint8_t* __restrict__ codes, int64_t rows, int K,
@@ -503,13 +596,15 @@ __global__ void unpack_codes_kernel(int fmt, const uint8_t* __restrict__ codes, 
 
 __global__ void unpack_scales_kernel(int fmt, const uint8_t* __restrict__ scales, int64_t rows, int64_t rows_pad, int K,
                                      void* __restrict__ out) {
-  const int ng = (fmt == kFmtMXFP4) ? K / 32 : K / 64;
+  const int ng = (fmt == kFmtMXFP4) ? K / 32 : (fmt == kFmtNVFP4 ? K / 16 : K / 64);
   const int64_t total = rows * ng;
   for (int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; d < total; d += int64_t(gridDim.x) * blockDim.x) {
     const int64_t r = d / ng;
     const int g = int(d % ng);
     if (fmt == kFmtMXFP4)
       reinterpret_cast<uint8_t*>(out)[d] = scales[mx_scale_byte(r, g, K)];
+    else if (fmt == kFmtNVFP4)
+      reinterpret_cast<uint8_t*>(out)[d] = scales[nv_scale_byte(r, g, K)];
     else
       reinterpret_cast<uint16_t*>(out)[d] = *reinterpret_cast<const uint16_t*>(scales + i4_scale_byte(r, g, rows_pad));
   }
@@ -591,18 +686,33 @@ hipError_t launch_quantize_act(int fmt, const uint16_t* X, int64_t rows, int64_t
   if (fmt == kFmtMXFP4)
     return launch_quantize_act_fmt<kFmtMXFP4>(X, rows, ld, K, lam, rlam, rlo, L1f, codes, scales, rows_pad, Dout, part,
                                               r_pad, kr, splits, wflags, s);
+  if (fmt == kFmtNVFP4)
+    return launch_quantize_act_fmt<kFmtNVFP4>(X, rows, ld, K, lam, rlam, rlo, L1f, codes, scales, rows_pad, Dout, part,
+                                              r_pad, kr, splits, wflags, s);
   return launch_quantize_act_fmt<kFmtINT4>(X, rows, ld, K, lam, rlam, rlo, L1f, codes, scales, rows_pad, Dout, part,
                                            r_pad, kr, splits, wflags, s);
 }
 
+static unsigned grid_for(int64_t total, int block);
+
+// NVFP4 first writes max |R| to amax_bits (the tensor scale's source).
 hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t ld, int K, uint8_t* codes,
-                                  uint8_t* scales, int64_t rows_pad, hipStream_t s) {
+                                  uint8_t* scales, int64_t rows_pad, uint32_t* amax_bits, hipStream_t s) {
   const int nw = pick_waves(K);
   const dim3 grid(unsigned(rows_pad / 16)), block(unsigned(64 * nw));
-  if (fmt == kFmtMXFP4)
-    hipLaunchKernelGGL((quantize_weight_kernel<kFmtMXFP4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad);
-  else
-    hipLaunchKernelGGL((quantize_weight_kernel<kFmtINT4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad);
+  if (fmt == kFmtMXFP4) {
+    hipLaunchKernelGGL((quantize_weight_kernel<kFmtMXFP4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad,
+                       amax_bits);
+  } else if (fmt == kFmtNVFP4) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, amax_bits);
+    hipLaunchKernelGGL(abs_max_kernel, dim3(grid_for(rows * (K / 4), 256)), dim3(256), 0, s, R, rows, ld, K,
+                       amax_bits);
+    hipLaunchKernelGGL((quantize_weight_kernel<kFmtNVFP4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad,
+                       amax_bits);
+  } else {
+    hipLaunchKernelGGL((quantize_weight_kernel<kFmtINT4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad,
+                       amax_bits);
+  }
   return hipGetLastError();
 }
 
