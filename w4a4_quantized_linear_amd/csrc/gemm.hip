@@ -1142,10 +1142,14 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     // 256 x 256 tiles when they fill the chip, else 128 x 128 tiles (up to two
     // workgroups per CU).  A last partial round of 256 x 256 tiles that fits in
     // one round of 128 x 128 quarters (two per CU) runs as quarters, in a second
-    // launch: half a big round instead of a whole one.
+    // launch: half a big round instead of a whole one.  A GELU epilogue is VALU
+    // work that leaves the matrix cores idle; with two 128 x 128 workgroups per
+    // CU one's epilogue can overlap the other's main loop, which measured
+    // slightly faster at the FLUX fc1 shape (about 1-2% in back-to-back runs on
+    // one device), so GELU layers take 128 x 128 tiles throughout.
     const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
     g.tile0 = -1;
-    if (big >= kMinBigTiles) {
+    if (big >= kMinBigTiles && !gelu) {
       int dev = 0, cus = 256;
       if (hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
