@@ -87,7 +87,7 @@ __host__ __device__ inline WeightLayout weight_layout(int fmt, int K, int N, int
 }
 
 constexpr int kActRowTiles = 8;        // 16-row tiles (one per wave) per activation workgroup
-constexpr int kActLdsBytes = 65536;    // LDS for one workgroup's lambda, r, rl and L1 fragments
+constexpr int kActLdsBytes = 81920;    // LDS for one workgroup's lambda, r, rl and L1 fragments (two fit a CU)
 constexpr int kActMinWorkgroups = 384; // fewer leave CUs idle
 
 // Work split of the activation kernel: a workgroup takes kActRowTiles 16-row
