@@ -115,13 +115,14 @@ def test_layer_elementwise(torch_dev, case):
 
 
 def test_tile_schedules_elementwise(torch_dev):
-    """The MXFP4 GEMM picks its tiles by the size of the output: 256 x 256 tiles,
-    a partial last round of them split into 128 x 128 quarters in a second
-    launch, or 128 x 128 tiles throughout.  Each schedule, element by element
-    against the oracle: 2048 x 8448 (264 big tiles: 256 + 8 split into 32
-    quarters), 1024 x 512 (8 big tiles: quarters only)."""
+    """The MXFP4 GEMM picks its tiles by the size of the output: 256 x 256 tiles
+    for 128 up to one round of them, else 128 x 128 tiles; both walk the output
+    in groups of 8 tile columns.  Each schedule, element by element against the
+    oracle, with a last raster group narrower than 8: 2048 x 4352 (136 big
+    tiles, 17 columns), 2048 x 8448 (264 big tiles: 128 x 128 tiles, 66
+    columns), 1024 x 512 (8 big tiles: 128 x 128 tiles, 4 columns)."""
     torch, dev = torch_dev
-    for (M, N, seed) in [(2048, 8448, 41), (1024, 512, 42)]:
+    for (M, N, seed) in [(2048, 4352, 43), (2048, 8448, 41), (1024, 512, 42)]:
         K = 512
         spec, L = _medium_layer("qkv", "mxfp4", M, K, N, 16, seed)
         layer = sq.Layer("mxfp4", K, N, 16)

@@ -34,10 +34,6 @@ struct GemmArgs {
   int K, N, r_pad;
   uint32_t epi;
   void* Y;
-  // MXFP4 with 128 x 128 tiles: -1 covers the whole output; t >= 0 covers the
-  // quarters of the 256 x 256 tiles t, t + 1, ... (in the tile order of the
-  // 256 x 256 launch, which took the tiles before t).
-  int tile0;
   // Fused QKV epilogue: Q/K normalization weights (bf16[128]), eps, and the
   // rotary cos / sin per token and pair (fp32, M x 64).
   const uint16_t* norm_q;
@@ -450,6 +446,8 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
+constexpr int kRasterCols = 8;   // output-column tiles per raster group (see gemm_mxfp4_kernel)
+
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
@@ -468,14 +466,15 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   int tm, tn;
   {
     const int t = xcd_remap(blockIdx.x, gridDim.x);
-    if (g.tile0 < 0) {
-      tm = t % tiles_m;
-      tn = t / tiles_m;
-    } else {                                       // quarter t % 4 of 256 x 256 tile tile0 + t / 4
-      const int tb = g.tile0 + t / 4, q = t % 4, tmb = int(g.M_pad / 256);
-      tm = (tb % tmb) * 2 + (q & 1);
-      tn = (tb / tmb) * 2 + (q >> 1);
-    }
+    // the grid covers the whole output: groups of kRasterCols output columns,
+    // consecutive tiles walking a group's columns first, then its rows, so the
+    // workgroups an XCD runs at once share a few weight and activation panels
+    // in that XCD's L2
+    const int tiles_n = int(g.N_pad / BN);
+    const int grp = t / (kRasterCols * tiles_m), in = t % (kRasterCols * tiles_m);
+    const int gcols = tiles_n - grp * kRasterCols < kRasterCols ? tiles_n - grp * kRasterCols : kRasterCols;
+    tn = grp * kRasterCols + in % gcols;
+    tm = in / gcols;
   }
   const int64_t nt0 = int64_t(tn) * (BN / 16);    // first 16-row weight tile of the workgroup
   const int64_t mt0 = int64_t(tm) * (BM / 16);
@@ -1139,34 +1138,23 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     else hipLaunchKernelGGL((KERNEL<WN, WM, false, false>), dim3(NB), dim3(THREADS), 0, s, g);              \
   } while (0)
   if (fmt == kFmtMXFP4) {
-    // 256 x 256 tiles when they fill the chip, else 128 x 128 tiles (up to two
-    // workgroups per CU).  A last partial round of 256 x 256 tiles that fits in
-    // one round of 128 x 128 quarters (two per CU) runs as quarters, in a second
-    // launch: half a big round instead of a whole one.  A GELU epilogue is VALU
-    // work that leaves the matrix cores idle; with two 128 x 128 workgroups per
-    // CU one's epilogue can overlap the other's main loop, which measured
-    // slightly faster at the FLUX fc1 shape (about 1-2% in back-to-back runs on
-    // one device), so GELU layers take 128 x 128 tiles throughout.
+    // 256 x 256 tiles (one workgroup per CU) when there are between kMinBigTiles
+    // and one round of them: fewer, larger tiles then keep more of the chip busy
+    // per byte staged.  Otherwise 128 x 128 tiles, two workgroups per CU: with
+    // the grouped raster their operand panels stay in L2, the last round is half
+    // as coarse, and one workgroup's epilogue (the VALU-bound GELU) overlaps the
+    // other's main loop.  Measured back to back on one device (us, big / small
+    // tiles): fc1 4608 x 3072 -> 12288 with GELU 125 / 121, QKV 4608 x 3072 ->
+    // 9216 90 / 84, fc2 4608 x 12288 -> 3072 (216 big tiles) 88 / 100.
     const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-    g.tile0 = -1;
-    if (big >= kMinBigTiles && !gelu) {
-      int dev = 0, cus = 256;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-      const unsigned rem = big % unsigned(cus), full = big - rem;
-      if (full > 0 && rem > 0 && rem * 4 <= 2 * unsigned(cus)) {
-        SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, full);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        g.tile0 = int(full);
-        SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, rem * 4);
-      } else {
-        SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
-      }
-    } else {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (big >= kMinBigTiles && big < unsigned(cus))
+      SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
+    else
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
-    }
   } else if (fmt == kFmtNVFP4) {
     const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
     SVDQ_LAUNCH(gemm_nvfp4_kernel, 4, 4, 256, nb);
@@ -1195,7 +1183,6 @@ hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const u
   g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
   g.epi = epi;
   g.Y = Y;
-  g.tile0 = -1;
   g.norm_q = norm_q; g.norm_k = norm_k; g.rope_cos = rope_cos; g.rope_sin = rope_sin; g.eps = eps;
   const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
   hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(nb), dim3(256), 0, s, g);
@@ -1216,7 +1203,6 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
   g.K = K; g.N = N; g.r_pad = int(wl.r_pad);
   g.epi = epi;
   g.Y = nullptr;
-  g.tile0 = -1;
   g.nblob = nblob;
   g.nact = nact;
   g.n_lam = nwl.lam; g.n_rlam = nwl.rlam; g.n_rlo = nwl.rlo; g.n_L1 = nwl.L1; g.n_flags = nwl.flags;
