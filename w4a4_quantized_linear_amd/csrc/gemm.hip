@@ -446,7 +446,18 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int kRasterCols = 8;   // output-column tiles per raster group (see gemm_mxfp4_kernel)
+// Tile order of a grid that covers the whole output (tiles_n x tiles_m tiles):
+// groups of kRasterCols output columns, consecutive tiles walking a group's
+// columns first, then its rows, so the workgroups an XCD runs at once (t from
+// xcd_remap: a contiguous range per XCD) share a few weight and activation
+// panels in that XCD's L2.
+constexpr int kRasterCols = 8;
+__device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int grp = t / (kRasterCols * tiles_m), in = t % (kRasterCols * tiles_m);
+  const int gcols = tiles_n - grp * kRasterCols < kRasterCols ? tiles_n - grp * kRasterCols : kRasterCols;
+  tn = grp * kRasterCols + in % gcols;
+  tm = in / gcols;
+}
 
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
@@ -466,15 +477,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   int tm, tn;
   {
     const int t = xcd_remap(blockIdx.x, gridDim.x);
-    // the grid covers the whole output: groups of kRasterCols output columns,
-    // consecutive tiles walking a group's columns first, then its rows, so the
-    // workgroups an XCD runs at once share a few weight and activation panels
-    // in that XCD's L2
-    const int tiles_n = int(g.N_pad / BN);
-    const int grp = t / (kRasterCols * tiles_m), in = t % (kRasterCols * tiles_m);
-    const int gcols = tiles_n - grp * kRasterCols < kRasterCols ? tiles_n - grp * kRasterCols : kRasterCols;
-    tn = grp * kRasterCols + in % gcols;
-    tm = in / gcols;
+    raster_tile(t, tiles_m, int(g.N_pad / BN), tm, tn);
   }
   const int64_t nt0 = int64_t(tn) * (BN / 16);    // first 16-row weight tile of the workgroup
   const int64_t mt0 = int64_t(tm) * (BM / 16);
@@ -659,8 +662,8 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = t % tiles_m, tn = t / tiles_m;
+  int tm, tn;
+  raster_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, int(g.N_pad / BN), tm, tn);
   const int64_t n0 = int64_t(tn) * BN + (w & 1) * (WN * 16);
   const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
   const int KS = g.K / kKStep;
@@ -788,8 +791,8 @@ __global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = t % tiles_m, tn = t / tiles_m;
+  int tm, tn;
+  raster_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, int(g.N_pad / BN), tm, tn);
   const int64_t n0 = int64_t(tn) * BN + (w & 1) * (WN * 16);
   const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
   const int KS = g.K / kKStep;
