@@ -574,7 +574,11 @@ __global__ void __launch_bounds__(256) abs_max_kernel(const float* __restrict__ 
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+  // one atomic per workgroup (a few hundred in all: many on one address serialize)
+  __shared__ float wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(out, __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
 }
 
 // ---- test-only unpackers to the canonical layout ----
@@ -705,8 +709,8 @@ hipError_t launch_quantize_weight(int fmt, const float* R, int64_t rows, int64_t
                        amax_bits);
   } else if (fmt == kFmtNVFP4) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, amax_bits);
-    hipLaunchKernelGGL(abs_max_kernel, dim3(grid_for(rows * (K / 4), 256)), dim3(256), 0, s, R, rows, ld, K,
-                       amax_bits);
+    const unsigned gm = grid_for(rows * (K / 4), 256);
+    hipLaunchKernelGGL(abs_max_kernel, dim3(gm < 512 ? gm : 512), dim3(256), 0, s, R, rows, ld, K, amax_bits);
     hipLaunchKernelGGL((quantize_weight_kernel<kFmtNVFP4>), grid, block, 0, s, R, rows, ld, K, codes, scales, rows_pad,
                        amax_bits);
   } else {
