@@ -44,7 +44,10 @@ def _oracle(Y_o, E):
                             E["cos"], E["sin"])
 
 
-@pytest.mark.parametrize("M,K,N,rank,seed", [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3)])
+# 128 x 128 tiles (a head split between two waves) in the first three; 256 x 256
+# tiles (192 of them, a head per wave) in the last
+@pytest.mark.parametrize("M,K,N,rank,seed", [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3),
+                                             (2048, 512, 6144, 16, 4)])
 def test_qkv_elementwise(torch_dev, M, K, N, rank, seed):
     torch, dev = torch_dev
     spec = synth.layer_spec("qkv", M=M, K=K, N=N, rank=rank, x_outliers=max(1, K // 100),

@@ -330,11 +330,15 @@ __device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, 
 // (bias included), one bf16 rounding at the store; V heads are stored as is.
 template <int WN, int WM>
 __device__ __forceinline__ void store_qkv(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
-                                          int64_t n0, int64_t m0, int lane, uint8_t* stage) {
-  static_assert(WN == 8, "a wave's 128 columns are one head");
+                                          int64_t n0, int64_t m0, int lane, int w, uint8_t* stage) {
+  // WN == 8: a wave's 128 columns are one head.  WN == 4: a head is the 128
+  // columns of the workgroup, split between waves w and w ^ 1, whose partial
+  // sums of squares meet in LDS.
+  static_assert(WN == 8 || WN == 4, "a head is one wave's or two waves' columns");
   const int q = lane >> 4;
   const int64_t hd = g.N / 3;
-  const int seg = int(n0 / hd);                 // 0: Q, 1: K, 2: V (uniform for the wave)
+  const int seg = int(n0 / hd);                 // 0: Q, 1: K, 2: V (uniform for the workgroup)
+  const int fo = int(n0 % 128);                 // the wave's first feature within its head
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -346,31 +350,53 @@ __device__ __forceinline__ void store_qkv(const GemmArgs& g, v4f (&acc)[WN][WM],
     float wv[WN][4];
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      const uint2 u = *reinterpret_cast<const uint2*>(wnorm + 16 * i + 4 * q);
+      const uint2 u = *reinterpret_cast<const uint2*>(wnorm + fo + 16 * i + 4 * q);
       wv[i][0] = bf_lo(u.x); wv[i][1] = bf_hi(u.x); wv[i][2] = bf_lo(u.y); wv[i][3] = bf_hi(u.y);
     }
-    // cos / sin of the lane's row in 16-row tile j: features 16 i + 4 q + e are
-    // pairs p = 8 i + 2 q (e = 0, 1) and p + 1 (e = 2, 3); loaded one tile ahead
+    // cos / sin of the lane's row in 16-row tile j: features fo + 16 i + 4 q + e
+    // are pairs p = fo / 2 + 8 i + 2 q (e = 0, 1) and p + 1 (e = 2, 3); loaded one
+    // tile ahead
     float2 cb[2][WN], sbuf[2][WN];
     auto load_rot = [&](int j, float2 (&c)[WN], float2 (&sn)[WN]) {
       const int64_t m = m0 + 16 * j + (lane & 15);
       const int64_t mc = m < g.M ? m : g.M - 1;  // rows past M are not stored
 #pragma unroll
       for (int i = 0; i < WN; ++i) {
-        c[i] = *reinterpret_cast<const float2*>(g.rope_cos + mc * 64 + 8 * i + 2 * q);
-        sn[i] = *reinterpret_cast<const float2*>(g.rope_sin + mc * 64 + 8 * i + 2 * q);
+        c[i] = *reinterpret_cast<const float2*>(g.rope_cos + mc * 64 + fo / 2 + 8 * i + 2 * q);
+        sn[i] = *reinterpret_cast<const float2*>(g.rope_sin + mc * 64 + fo / 2 + 8 * i + 2 * q);
       }
     };
-    load_rot(0, cb[0], sbuf[0]);
-#pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      if (j + 1 < WM) load_rot(j + 1, cb[(j + 1) & 1], sbuf[(j + 1) & 1]);
+    // sum of squares of each token's features in this wave
+    auto sumsq = [&](int j) {
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < WN; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss = fmaf(acc[i][j][e], acc[i][j][e], ss);
-      ss = rowgroup_sum(ss);
+      return rowgroup_sum(ss);
+    };
+    // WN == 4: plus the partner wave's half of the head, through LDS
+    float ssum[WN == 4 ? WM : 1];
+    if constexpr (WN == 4) {
+      __shared__ float part_ss[4][WM][16];
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        ssum[j] = sumsq(j);
+        if (q == 0) part_ss[w][j][lane & 15] = ssum[j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < WM; ++j) ssum[j] += part_ss[w ^ 1][j][lane & 15];
+    }
+    load_rot(0, cb[0], sbuf[0]);
+#pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      if (j + 1 < WM) load_rot(j + 1, cb[(j + 1) & 1], sbuf[(j + 1) & 1]);
+      float ss;
+      if constexpr (WN == 4)
+        ss = ssum[j];
+      else
+        ss = sumsq(j);
       const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + g.eps);
 #pragma unroll
       for (int i = 0; i < WN; ++i) {
@@ -463,7 +489,7 @@ template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = fal
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(QOUT < 0 || WN == 8, "the fused quantization takes 256 x 256 tiles");
-  static_assert(!QKV || (WN == 8 && QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue takes 128-column heads");
+  static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   constexpr int SF = 2 * WN;            // fragments per operand per stage
   constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
   constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
@@ -620,7 +646,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
-    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
     epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
@@ -1120,6 +1146,16 @@ hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K
 
 constexpr unsigned kMinBigTiles = 128;   // MXFP4: fewer 256 x 256 tiles than this -> 128 x 128 tiles
 
+// The MXFP4 tile choice (see launch_gemm): 256 x 256 tiles for kMinBigTiles up
+// to one round of them on this device's CUs, else 128 x 128 tiles.
+static bool use_big_tiles(unsigned big) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return big >= kMinBigTiles && big < unsigned(cus);
+}
+
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
   GemmArgs g{};
@@ -1150,11 +1186,7 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     // tiles): fc1 4608 x 3072 -> 12288 with GELU 125 / 121, QKV 4608 x 3072 ->
     // 9216 90 / 84, fc2 4608 x 12288 -> 3072 (216 big tiles) 88 / 100.
     const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (big >= kMinBigTiles && big < unsigned(cus))
+    if (use_big_tiles(big))
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
     else
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
@@ -1187,8 +1219,11 @@ hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const u
   g.epi = epi;
   g.Y = Y;
   g.norm_q = norm_q; g.norm_k = norm_k; g.rope_cos = rope_cos; g.rope_sin = rope_sin; g.eps = eps;
-  const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-  hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(nb), dim3(256), 0, s, g);
+  const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+  if (use_big_tiles(big))
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(big), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, -1, true>), dim3(big * 4), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
