@@ -354,7 +354,7 @@ def fused_pair(args, sq, torch, layers, weights, x, ws, outs, epis, M, flops):
                         "down-projection sum); fc2 gemm"}
 
 
-def cpu_baseline(specs, budget_rows=1024):
+def cpu_baseline(specs, budget_rows=2048):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     `budget_rows` tokens of each layer against 1/2 (K <= 4096) or 1/8 of the
     output columns (about 10 s of host time), scaled to effective TOPS of the
