@@ -115,12 +115,13 @@ def test_layer_elementwise(torch_dev, case):
 
 
 def test_tile_schedules_elementwise(torch_dev):
-    """The MXFP4 GEMM picks its tiles by the size of the output: 256 x 256 tiles
-    for 128 up to one round of them, else 128 x 128 tiles; both walk the output
-    in groups of 8 tile columns.  Each schedule, element by element against the
-    oracle, with a last raster group narrower than 8: 2048 x 4352 (136 big
-    tiles, 17 columns), 2048 x 8448 (264 big tiles: 128 x 128 tiles, 66
-    columns), 1024 x 512 (8 big tiles: 128 x 128 tiles, 4 columns)."""
+    """The MXFP4 GEMM picks its tiles by the size of the output: 256-wide tiles
+    for 128 up to one round of 256 x 256 ones, else 128 x 128 tiles; both walk
+    the output in groups of 8 tile columns.  Each schedule, element by element
+    against the oracle, with a last raster group narrower than 8: 2048 x 4352
+    (136 big tiles, 17 columns: 187 tiles of 256 x 192), 2048 x 8448 (264 big
+    tiles: 128 x 128 tiles, 66 columns), 1024 x 512 (8 big tiles: 128 x 128
+    tiles, 4 columns)."""
     torch, dev = torch_dev
     for (M, N, seed) in [(2048, 4352, 43), (2048, 8448, 41), (1024, 512, 42)]:
         K = 512
@@ -132,6 +133,32 @@ def test_tile_schedules_elementwise(torch_dev):
         torch.cuda.synchronize()
         ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")
         check_fp32_output(Y.cpu().numpy(), ref["Y"], f"M={M} N={N}")
+
+
+def test_short_tiles_elementwise(torch_dev):
+    """256-wide tiles shorter than 256 rows, chosen when they fill more CUs in
+    one round: 4600 x 3072 (12 tile columns: 252 tiles of 224 rows, the last
+    one past the padded rows) and 2048 x 4352 (17 columns: 187 tiles of 192
+    rows).  fp32, bf16 and GELU outputs element by element against the oracle;
+    bf16 must be the round-to-nearest-even of fp32 (the odd last block of a
+    224-row tile goes through the store staging alone)."""
+    torch, dev = torch_dev
+    for (M, N, seed) in [(4600, 3072, 44), (2048, 4352, 45)]:
+        K = 512
+        spec, L = _medium_layer("qkv", "mxfp4", M, K, N, 32, seed)
+        layer = sq.Layer("mxfp4", K, N, 32)
+        print(f"short tiles M={M} N={N}", flush=True)
+        w = pack(layer, L, torch, dev)
+        ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+        Yf = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+        Yb = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS)
+        Yg = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU)
+        torch.cuda.synchronize()
+        ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")
+        check_fp32_output(Yf.cpu().numpy(), ref["Y"], f"M={M} N={N} fp32")
+        check_bf16_output(bf16_to_np(Yb), ref["Y"], f"M={M} N={N} bf16")
+        assert np.array_equal(Yb.cpu().view(torch.int16).numpy().view(np.uint16), F.bf16_bits(Yf.cpu().numpy()))
+        check_bf16_output(bf16_to_np(Yg), Ly.gelu(ref["Y"]), f"M={M} N={N} GELU bf16")
 
 
 def test_gelu_epilogue_pointwise(torch_dev):

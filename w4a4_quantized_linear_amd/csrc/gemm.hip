@@ -66,12 +66,14 @@ __device__ __forceinline__ void add_lowrank(const GemmArgs& g, v4f (&acc)[WN][WM
   const int R32 = g.r_pad / 32;
   const uint4* L2f = reinterpret_cast<const uint4*>(g.wblob + g.w_L2) + (n0 / 16) * R32 * 64 + lane;
   const uint4* Df = reinterpret_cast<const uint4*>(g.act + g.a_D) + (m0 / 16) * R32 * 128 + lane;
+  const int64_t jend = g.M_pad / 16 - m0 / 16;   // blocks of this wave inside the padded rows
   for (int r32 = 0; r32 < R32; ++r32) {
     uint4 l2[WN];
 #pragma unroll
     for (int i = 0; i < WN; ++i) l2[i] = L2f[(i * R32 + r32) * 64];
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
+      if (j >= jend) break;
       const uint4 dh = Df[(j * R32 + r32) * 128];
       const uint4 dl = Df[(j * R32 + r32) * 128 + 64];
 #pragma unroll
@@ -97,8 +99,8 @@ __device__ __forceinline__ void load_bias(const GemmArgs& g, int64_t n0, int lan
 }
 
 // Y = act(acc (+ bias)) for the wave tile.  fp32 output: one 16-byte store per
-// lane and block.  bf16 output: each pair of 16-row blocks goes through the
-// wave's LDS staging area so that every store instruction writes whole
+// lane and block.  bf16 output: each pair of 16-row blocks (the last block alone
+// when their number is odd) goes through the wave's LDS staging area so that every store instruction writes whole
 // 256-byte row segments.
 template <int WN, int WM, bool OUT_F32, bool GELU, bool ADD_BIAS>
 __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
@@ -128,11 +130,12 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM],
     constexpr int RB = stage_row_bytes<WN>();
     constexpr int LPR = WN * 2;          // lanes per row (16 bytes each)
     constexpr int RPI = 64 / LPR;        // rows per store instruction
-    static_assert(WM % 2 == 0 && 32 % RPI == 0, "wave tile shape");
+    static_assert(16 % RPI == 0, "wave tile shape");
 #pragma unroll
-    for (int jp = 0; jp < WM / 2; ++jp) {
+    for (int jp = 0; jp < (WM + 1) / 2; ++jp) {
+      const int nj = 2 * jp + 2 <= WM ? 2 : 1;   // blocks in this pair (1 for the last of an odd count)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+      for (int jj = 0; jj < nj; ++jj) {
         const int j = 2 * jp + jj;
         uint8_t* row = stage + (jj * 16 + (lane & 15)) * RB + (lane >> 4) * 8;
 #pragma unroll
@@ -143,7 +146,7 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM],
         }
       }
 #pragma unroll
-      for (int r = 0; r < 32 / RPI; ++r) {
+      for (int r = 0; r < nj * 16 / RPI; ++r) {
         const int rr = r * RPI + lane / LPR;
         const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * RB + (lane % LPR) * 16);
         const int64_t m = m0 + jp * 32 + rr;
@@ -485,11 +488,13 @@ __device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int
   tm = in / gcols;
 }
 
-template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false>
+template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(QOUT < 0 || WN == 8, "the fused quantization takes 256 x 256 tiles");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
+  // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
+  static_assert(WMA == WM || (WN == 8 && QOUT < 0 && !QKV && WMA > WM / 2 && WMA < WM), "short tiles");
   constexpr int SF = 2 * WN;            // fragments per operand per stage
   constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
   constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
@@ -498,8 +503,8 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = w & 1, wm = w >> 1;               // 2 x 2 waves
-  constexpr int BN = 32 * WN, BM = 32 * WM;
-  const int tiles_m = int(g.M_pad / BM);
+  constexpr int BN = 32 * WN, BM = 32 * WMA;
+  const int tiles_m = int((g.M_pad + BM - 1) / BM);
   int tm, tn;
   {
     const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -509,26 +514,32 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   const int64_t mt0 = int64_t(tm) * (BM / 16);
   const int KS = g.K / kKStep, KSUP = g.K / kKSuper;
   const int64_t n0 = (nt0 + wn * WN) * 16;
-  const int64_t m0 = (mt0 + wm * WM) * 16;
+  const int64_t m0 = (mt0 + wm * WMA) * 16;
   auto slot = [&](int u) -> uint4* { return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3; };
 
   // Per-workgroup views of the operands: SF row tiles of codes and of scales each.
+  // A stage always holds SF activation fragments; with short tiles the last
+  // 2 (WM - WMA) are not read, and the view stops at the padded rows (loads
+  // past it return zeros; those rows are never stored).
+  const int64_t act_rt = g.M_pad / 16 - mt0 < SF ? g.M_pad / 16 - mt0 : SF;
   const uint32_t code_bytes = uint32_t(SF) * KS * 1024, scale_bytes = uint32_t(SF) * KSUP * 256;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.wblob + g.w_codes + size_t(nt0) * KS * 1024, code_bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.act + g.a_codes + size_t(mt0) * KS * 1024, code_bytes);
+  const __amdgpu_buffer_rsrc_t rB =
+      make_rsrc(g.act + g.a_codes + size_t(mt0) * KS * 1024, uint32_t(act_rt) * KS * 1024);
   const __amdgpu_buffer_rsrc_t rSA = make_rsrc(g.wblob + g.w_scales + size_t(nt0) * KSUP * 256, scale_bytes);
-  const __amdgpu_buffer_rsrc_t rSB = make_rsrc(g.act + g.a_scales + size_t(mt0) * KSUP * 256, scale_bytes);
+  const __amdgpu_buffer_rsrc_t rSB =
+      make_rsrc(g.act + g.a_scales + size_t(mt0) * KSUP * 256, uint32_t(act_rt) * KSUP * 256);
   const uint32_t voff16 = uint32_t(lane) * 16, voff4 = uint32_t(lane) * 4;
 
   // E8M0 scales of this wave's 8 weight tiles and 8 activation tiles, one superfragment
-  uint32_t sa[WN], sb[WM], san[WN], sbn[WM];
-  auto load_scales = [&](uint32_t (&x)[WN], uint32_t (&y)[WM], int sup) {
+  uint32_t sa[WN], sb[WMA], san[WN], sbn[WMA];
+  auto load_scales = [&](uint32_t (&x)[WN], uint32_t (&y)[WMA], int sup) {
 #pragma unroll
     for (int i = 0; i < WN; ++i)
       x[i] = __builtin_amdgcn_raw_buffer_load_b32(rSA, voff4, uint32_t((wn * WN + i) * KSUP + sup) * 256, 0);
 #pragma unroll
-    for (int j = 0; j < WM; ++j)
-      y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WM + j) * KSUP + sup) * 256, 0);
+    for (int j = 0; j < WMA; ++j)
+      y[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, voff4, uint32_t((wm * WMA + j) * KSUP + sup) * 256, 0);
   };
   // This wave's share of a stage: weight fragments PW w .. PW w + PW-1 (f < PW)
   // and the activation fragments of the same numbers (PW <= f < 2 PW).
@@ -539,14 +550,14 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     load_frag_lds(wt ? rA : rB, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
   };
   auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
-  auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WM + j) * 64 + lane]; };
+  auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WMA + j) * 64 + lane]; };
 
   // Prologue: scales of superfragment 0, then stages 0..2 into slots 0..2.
-  v4f acc[WN][WM];
+  v4f acc[WN][WMA];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WMA; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   load_scales(sa, sb, 0);
 #pragma unroll
   for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
@@ -560,7 +571,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   // fb[4..7] of the same stage; half 1 uses fb[4..7] and meanwhile reads the
   // next stage's fb[0..3] and, after row i, fa[i].  So every fragment is read
   // while the MFMAs of another one run, and the reads spread over the step.
-  uint4 fa[WN], fb[WM];
+  uint4 fa[WN], fb[WMA];
 #pragma unroll
   for (int j = 0; j < WM / 2; ++j) fb[j] = frag_b(ring0, j);
 #pragma unroll
@@ -584,11 +595,11 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
       if (FETCH) fetch1(s3, step + 3, i);                                                             \
       _Pragma("unroll") for (int j = 0; j < WM / 2; ++j)                                              \
         acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
-      if (i % 2 == 1) fb[WM / 2 + i / 2] = frag_b(s0, WM / 2 + i / 2);                                \
+      if (i % 2 == 1 && WM / 2 + i / 2 < WMA) fb[WM / 2 + i / 2] = frag_b(s0, WM / 2 + i / 2);        \
       __builtin_amdgcn_sched_barrier(0);                                                              \
     }                                                                                                 \
     _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
-      _Pragma("unroll") for (int j = WM / 2; j < WM; ++j)                                             \
+      _Pragma("unroll") for (int j = WM / 2; j < WMA; ++j)                                            \
         acc[i][j] = mfma_fp4_sel<(U)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                         \
       if (READ) {                                                                                     \
         fa[i] = frag_a(s1, i);                                                                        \
@@ -604,13 +615,13 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   for (; sup + 1 < KSUP; ++sup) {
     const int t0 = sup * 4;
     SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
-    SVDQ_FP4_STEP(1, true, true, true, 2 * PW + WN + WM)
+    SVDQ_FP4_STEP(1, true, true, true, 2 * PW + WN + WMA)
     SVDQ_FP4_STEP(2, true, true, false, 2 * PW)
     SVDQ_FP4_STEP(3, true, true, false, 2 * PW)
 #pragma unroll
     for (int i = 0; i < WN; ++i) sa[i] = san[i];
 #pragma unroll
-    for (int j = 0; j < WM; ++j) sb[j] = sbn[j];
+    for (int j = 0; j < WMA; ++j) sb[j] = sbn[j];
   }
   {
     const int t0 = sup * 4;
@@ -648,7 +659,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     load_bias<WN>(g, n0, lane, bv);
     store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
-    epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+    epilogue<WN, WMA, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
 }
 
@@ -1146,14 +1157,36 @@ hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K
 
 constexpr unsigned kMinBigTiles = 128;   // MXFP4: fewer 256 x 256 tiles than this -> 128 x 128 tiles
 
-// The MXFP4 tile choice (see launch_gemm): 256 x 256 tiles for kMinBigTiles up
-// to one round of them on this device's CUs, else 128 x 128 tiles.
-static bool use_big_tiles(unsigned big) {
+static int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  return big >= kMinBigTiles && big < unsigned(cus);
+  return cus;
+}
+
+// The MXFP4 tile choice (see launch_gemm): 256 x 256 tiles for kMinBigTiles up
+// to one round of them on this device's CUs, else 128 x 128 tiles.
+static bool use_big_tiles(unsigned big) { return big >= kMinBigTiles && big < unsigned(device_cus()); }
+
+// Height of the 256-wide tiles, as activation blocks of 16 rows per wave (the
+// tile is 32 wma rows): the fewest rounds of workgroups on the CUs times the
+// rows per tile, the taller tile on a tie.  FLUX fc2 (4608 rows, 12 tile
+// columns): 216 tiles of 256 rows leave 40 of 256 CUs idle, 252 tiles of 224
+// rows fill them, each with 7/8 of the work.
+static int short_tile_blocks(int64_t tiles_n, int64_t M_pad) {
+  const int64_t cus = device_cus();
+  int best = 8;
+  int64_t best_cost = 0;
+  for (int w = 8; w >= 6; --w) {
+    const int64_t tiles = tiles_n * ((M_pad + 32 * w - 1) / (32 * w));
+    const int64_t cost = (tiles + cus - 1) / cus * w;
+    if (w == 8 || cost < best_cost) {
+      best = w;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
@@ -1185,11 +1218,28 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     // other's main loop.  Measured back to back on one device (us, big / small
     // tiles): fc1 4608 x 3072 -> 12288 with GELU 125 / 121, QKV 4608 x 3072 ->
     // 9216 90 / 84, fc2 4608 x 12288 -> 3072 (216 big tiles) 88 / 100.
+    //
+    // 256-wide tiles may be shorter than 256 rows (short_tile_blocks), so that
+    // one round fills more CUs: fc2 on 252 tiles of 224 rows takes 89 us
+    // against 94 on 216 tiles of 256 (alternating runs on one device).
     const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-    if (use_big_tiles(big))
-      SVDQ_LAUNCH(gemm_mxfp4_kernel, 8, 8, 256, big);
-    else
+    if (use_big_tiles(big)) {
+      const int wma = short_tile_blocks(wl.N_pad / 256, al.M_pad);
+      const unsigned nb = unsigned((wl.N_pad / 256) * ((al.M_pad + 32 * wma - 1) / (32 * wma)));
+#define SVDQ_SHORT(WMA)                                                                                          \
+  do {                                                                                                           \
+    if (f32 && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
+    else if (f32) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
+    else if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
+    else hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
+  } while (0)
+      if (wma == 8) SVDQ_SHORT(8);
+      else if (wma == 7) SVDQ_SHORT(7);
+      else SVDQ_SHORT(6);
+#undef SVDQ_SHORT
+    } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
+    }
   } else if (fmt == kFmtNVFP4) {
     const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
     SVDQ_LAUNCH(gemm_nvfp4_kernel, 4, 4, 256, nb);
