@@ -142,8 +142,8 @@ svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void
  * as svdq_gemm would store it, then smooths, quantizes and packs H for dn into
  * an_packed as svdq_quantize_act(dn, wn_packed, H, M, ...) would: the same codes
  * and scales bit for bit, and D' = H_hat L1' summed in a different (fixed) order
- * (one fp32 partial per 256 columns of H, added in column order by a second
- * launch).  svdq_gemm(dn, wn_packed, an_packed, ...) then completes dn.  H itself
+ * (one fp32 partial per output tile column of H, 128 or 256 columns, added in
+ * column order by a second launch).  svdq_gemm(dn, wn_packed, an_packed, ...) then completes dn.  H itself
  * is never written.
  *   d, w_packed, a_packed  layer d as for svdq_gemm (a_packed from svdq_quantize_act)
  *   epi       SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU (no SVDQ_EPI_OUT_F32)

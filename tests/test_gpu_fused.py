@@ -22,13 +22,16 @@ pytestmark = pytest.mark.gpu
 EPI1 = sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU
 EPI2 = sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32
 
-# (M, K1, N1 = K2, rank1, N2, rank2, seed): ragged M, several 256-column tiles of
-# H, next-layer ranks 0 / 16 / 32 / 48, one row
+# (M, K1, N1 = K2, rank1, N2, rank2, seed): ragged M, several tile columns of H,
+# next-layer ranks 0 / 16 / 32 / 48, one row.  The fused GEMM takes the plain
+# GEMM's tiles: 128 x 128 for these (fewer than 128 tiles of 256 x 256), except
+# the 2048-row case (144 tiles of 256 x 256).
 CASES = [
     (300, 1024, 1024, 16, 512, 32, 1),
     (513, 512, 2048, 32, 256, 48, 2),
     (64, 1024, 512, 0, 1024, 0, 3),
     (1, 512, 512, 32, 512, 16, 4),
+    (2048, 512, 4608, 32, 256, 16, 6),
 ]
 
 

@@ -163,32 +163,35 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM],
 // SVDQuant and Nunchaku", names fused GELU/MLP kernels among the original
 // engine's model-specific paths).  H = bf16(act(acc + b)) is the next layer's
 // input X (its K is this layer's N).  Instead of storing H, the workgroup
-// quantizes its 256 x 256 tile of H for the next layer exactly as the
-// activation kernel does with H read from memory (same rounding of H, same
-// quotients, group maxima, scales and codes), and writes its tile's share of
-// the next layer's down projection H_hat L1' as one fp32 partial per 256
-// columns of H (summed in column order by a second launch).
+// quantizes its tile of H (256 x 256 or 128 x 128) for the next layer exactly
+// as the activation kernel does with H read from memory (same rounding of H,
+// same quotients, group maxima, scales and codes), and writes its tile's share
+// of the next layer's down projection H_hat L1' as one fp32 partial per tile
+// column (summed in column order by a second launch).
 //
-// Phase 1: each wave writes its 128 x 128 block of H (bf16) into LDS, the
-// workgroup's 256 rows x 256 columns in the four ring slots (64 rows each,
-// 512 bytes per row, 16-byte chunks swizzled by the row against bank
-// conflicts).  Phase 2: wave w quantizes rows 64 w .. 64 w + 63 from LDS in the
+// Phase 1: each wave writes its block of H (bf16) into LDS, the workgroup's
+// TC = 32 WN columns of each row in 64-row ring slots (TC * 2 bytes per row,
+// 16-byte chunks swizzled by the row against bank conflicts).  Phase 2: wave
+// w quantizes rows 8 WM w .. 8 WM w + 8 WM - 1 of the tile from LDS in the
 // activation kernel's lane layout (lane = row % 16 + 16 c holds 8 consecutive
 // elements of each 32-block), 64 columns per step.
 
 // Byte offset of bf16 element (row % 64, column k) of the tile in its slot.
+template <int WN>
 __device__ __forceinline__ uint32_t htile_off(int row, int k) {
-  return uint32_t((row & 63) * 512 + (((k >> 3) ^ (row & 31)) << 4) + (k & 7) * 2);
+  constexpr int CH = 4 * WN;                        // 16-byte chunks per row
+  return uint32_t((row & 63) * (CH * 16) + (((k >> 3) ^ (row & (CH - 1))) << 4) + (k & 7) * 2);
 }
 
 template <int WN, int WM, bool GELU>
 __device__ __forceinline__ void stage_h(v4f (&acc)[WN][WM], const float (&bv)[WN][4], int lane, int wn, int wm,
-                                        uint8_t* lo0, uint8_t* lo1, uint8_t* hi0, uint8_t* hi1) {
+                                        uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
   const int q = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
-    const int row = wm * 128 + j * 16 + r;           // row within the workgroup tile
-    uint8_t* const sl = wm == 0 ? (j < 4 ? lo0 : lo1) : (j < 4 ? hi0 : hi1);   // slot (row / 64)
+    const int row0 = wm * 16 * WM + j * 16;          // first row of the block within the workgroup tile
+    const int si = row0 >> 6;                        // its slot
+    uint8_t* const sl = si == 0 ? s0 : si == 1 ? s1 : si == 2 ? s2 : s3;
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
       float y[4];
@@ -197,53 +200,58 @@ __device__ __forceinline__ void stage_h(v4f (&acc)[WN][WM], const float (&bv)[WN
         y[e] = acc[i][j][e] + bv[i][e];
         if (GELU) y[e] = gelu_erf(y[e]);
       }
-      *reinterpret_cast<uint2*>(sl + htile_off(row, wn * 128 + i * 16 + q * 4)) =
+      *reinterpret_cast<uint2*>(sl + htile_off<WN>(row0 + r, wn * 16 * WN + i * 16 + q * 4)) =
           make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
     }
   }
 }
 
 // The next layer's L1' fragments (B operands of its down projection) for the
-// tile's 8 32-blocks and R16 rank tiles, into registers ahead of phase 2 (so
+// tile's NB 32-blocks and R16 rank tiles, into registers ahead of phase 2 (so
 // that no global load, which would also wait for the stores before it, sits
 // inside phase 2).
-template <int R16>
-__device__ __forceinline__ void load_l1_next(const GemmArgs& g, int k0, int lane, uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+template <int R16, int NB>
+__device__ __forceinline__ void load_l1_next(const GemmArgs& g, int k0, int lane, uint4 (&l1r)[NB][R16 > 0 ? R16 : 1]) {
   const uint4* const l1f = reinterpret_cast<const uint4*>(g.nblob + g.n_L1);
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+  for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int cb = 0; cb < R16; ++cb) l1r[kb][cb] = l1f[(size_t(k0 / 32 + kb) * R16 + cb) * 64 + lane];
 }
 
-// Phase 2 loop for wave w: rows mrow0 .. mrow0 + 63 of the tile (slot w).  lamv
-// holds lambda, 1/lambda and the correction term of the tile's 256 columns
-// (the next layer's K range k0 .. k0 + 255).  FAST: every quotient by the
-// two-operation form fma(x, r, x rl); otherwise by IEEE division.  Both give
-// the correctly rounded quotient wherever FAST is chosen (see quant_h).
-template <int R16, bool FAST>
-__device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slot, const float* lamv, int lane,
-                                           int64_t mrow0, int k0, int tn, const uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+// Phase 2 loop for wave w: rows mrow0 .. mrow0 + 8 WN - 1 of the output, rows
+// rbase .. of the slot.  lamv holds lambda, 1/lambda and the correction term of
+// the tile's TC columns (the next layer's K range k0 .. k0 + TC - 1).  FAST:
+// every quotient by the two-operation form fma(x, r, x rl); otherwise by IEEE
+// division.  Both give the correctly rounded quotient wherever FAST is chosen
+// (see quant_h).
+template <int WN, int R16, bool FAST>
+__device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slot, int rbase, const float* lamv,
+                                           int lane, int64_t mrow0, int k0, int tn,
+                                           const uint4 (&l1r)[WN][R16 > 0 ? R16 : 1]) {
+  constexpr int TC = 32 * WN;                       // columns of the tile
+  constexpr int RT = WN / 2;                        // 16-row tiles per wave (8 WN rows)
+  constexpr int ST = TC / 64;                       // 64-column steps
   const int r = lane & 15, c = lane >> 4;
   const int K2 = g.N;
   uint8_t* const codes = g.nact + g.n_codes;
   uint8_t* const scales = g.nact + g.n_scales;
   float* const part = reinterpret_cast<float*>(g.nact + g.n_part);
   const float* const slam = lamv;
-  const float* const srl = lamv + 256;
-  const float* const srlo = lamv + 512;
+  const float* const srl = lamv + TC;
+  const float* const srlo = lamv + 2 * TC;
 
-  for (int t = 0; t < 4; ++t) {                     // the wave's four 16-row tiles
-    const int row = t * 16 + r;                      // row within the slot
-    const int64_t m = mrow0 + row;
+  for (int t = 0; t < RT; ++t) {                    // the wave's 16-row tiles
+    const int row = rbase + t * 16 + r;              // row within the slot
+    const int64_t m = mrow0 + t * 16 + r;
     v4f dacc[R16 > 0 ? R16 : 1];
 #pragma unroll
     for (int cb = 0; cb < R16; ++cb) dacc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {                    // 64 columns per step
+    for (int s = 0; s < ST; ++s) {                   // 64 columns per step
       float ah[2][8], x[16];
-      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off(row, s * 64 + c * 8)), ah[0]);
-      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off(row, s * 64 + 32 + c * 8)), ah[1]);
+      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off<WN>(row, s * 64 + c * 8)), ah[0]);
+      unpack_bf8(*reinterpret_cast<const uint4*>(slot + htile_off<WN>(row, s * 64 + 32 + c * 8)), ah[1]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kl = s * 64 + (e >> 3) * 32 + c * 8 + (e & 7);
@@ -303,23 +311,24 @@ __device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slo
 // magnitude (the activation kernel's conditions); a first pass over the wave's
 // rows checks the values, and a wave with any value outside takes IEEE division
 // for all of its rows (same quotients, slower).
-template <int R16>
-__device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, const float* lamv, int lane,
-                                        int64_t mrow0, int k0, int tn, const uint4 (&l1r)[8][R16 > 0 ? R16 : 1]) {
+template <int WN, int R16>
+__device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, int rbase, const float* lamv, int lane,
+                                        int64_t mrow0, int k0, int tn, const uint4 (&l1r)[WN][R16 > 0 ? R16 : 1]) {
   const int r = lane & 15, c = lane >> 4;
   const uint32_t wf = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(g.nblob + g.n_flags));
   bool oor = false;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < WN / 2; ++t)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      oor = oor || exp_out_of_range(*reinterpret_cast<const uint4*>(slot + htile_off(t * 16 + r, s * 64 + c * 8)),
-                                    *reinterpret_cast<const uint4*>(slot + htile_off(t * 16 + r, s * 64 + 32 + c * 8)));
+    for (int s = 0; s < WN / 2; ++s)
+      oor = oor ||
+            exp_out_of_range(*reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + c * 8)),
+                             *reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + 32 + c * 8)));
   const bool fast = (wf & (kLamRangeBit | kDivSlowBit)) == 0 && !__any(oor);
   if (__builtin_expect(fast, 1))
-    quant_rows<R16, true>(g, slot, lamv, lane, mrow0, k0, tn, l1r);
+    quant_rows<WN, R16, true>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
   else
-    quant_rows<R16, false>(g, slot, lamv, lane, mrow0, k0, tn, l1r);
+    quant_rows<WN, R16, false>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
 }
 
 // Fused QKV epilogue (the next row after the layer: the Nunchaku in Diffusers
@@ -491,7 +500,6 @@ __device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
-  static_assert(QOUT < 0 || WN == 8, "the fused quantization takes 256 x 256 tiles");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
   static_assert(WMA == WM || (WN == 8 && QOUT < 0 && !QKV && WMA > WM / 2 && WMA < WM), "short tiles");
@@ -634,25 +642,26 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   // every wave passed the last barrier with no load in flight: the ring is free
   // for the output staging (one slot per wave)
   if constexpr (QOUT >= 0) {                        // QOUT = the next layer's rank tiles of 16
-    // lambda, 1/lambda and the correction of the next layer for this tile's 256 columns
-    __shared__ float lamv[3 * 256];
-    {
+    // lambda, 1/lambda and the correction of the next layer for this tile's BN columns
+    __shared__ float lamv[3 * BN];
+    if (int(threadIdx.x) < BN) {
       const int k = int(threadIdx.x);
       const int64_t kn = nt0 * 16 + k;
       lamv[k] = reinterpret_cast<const float*>(g.nblob + g.n_lam)[kn];
-      lamv[256 + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlam)[kn];
-      lamv[512 + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlo)[kn];
+      lamv[BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlam)[kn];
+      lamv[2 * BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlo)[kn];
     }
     add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
-    uint4 l1r[8][QOUT > 0 ? QOUT : 1];
-    load_l1_next<QOUT>(g, int(nt0 * 16), lane, l1r);
+    uint4 l1r[WN][QOUT > 0 ? QOUT : 1];
+    load_l1_next<QOUT, WN>(g, int(nt0 * 16), lane, l1r);
     stage_h<WN, WM, GELU>(acc, bv, lane, wn, wm, reinterpret_cast<uint8_t*>(ring0), reinterpret_cast<uint8_t*>(ring1),
                           reinterpret_cast<uint8_t*>(ring2), reinterpret_cast<uint8_t*>(ring3));
     __syncthreads();
-    quant_h<QOUT>(g, reinterpret_cast<const uint8_t*>(slot(w)), lamv, lane, mt0 * 16 + w * 64, int(nt0 * 16), tn,
-                  l1r);
+    const int prow = w * 8 * WM;                     // the wave's first row of the tile
+    quant_h<WN, QOUT>(g, reinterpret_cast<const uint8_t*>(slot(prow >> 6)), prow & 63, lamv, lane, mt0 * 16 + prow,
+                      int(nt0 * 16), tn, l1r);
   } else if constexpr (QKV) {
     add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
@@ -1296,11 +1305,19 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
   g.n_lam = nwl.lam; g.n_rlam = nwl.rlam; g.n_rlo = nwl.rlo; g.n_L1 = nwl.L1; g.n_flags = nwl.flags;
   g.n_codes = nal.codes; g.n_scales = nal.scales; g.n_part = nal.part;
   g.nr_pad = int(nwl.r_pad);
-  const unsigned nb = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+  // The plain GEMM's tile choice: 256 x 256 tiles for 128 up to one round of
+  // them, else 128 x 128 tiles (two workgroups per CU, so that one's
+  // quantization overlaps the other's main loop).
+  const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
+  const bool bigt = use_big_tiles(big);
+  const unsigned nb = bigt ? big : big * 4;
+  const int tile_cols = bigt ? 256 : 128;
   const bool gelu = (epi & SVDQ_EPI_GELU) != 0;
-#define SVDQ_QLAUNCH(R16)                                                                                    \
-  if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
-  else hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, R16>), dim3(nb), dim3(256), 0, s, g)
+#define SVDQ_QLAUNCH(R16)                                                                                        \
+  if (bigt && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
+  else if (bigt) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, R16>), dim3(nb), dim3(256), 0, s, g);  \
+  else if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, true, R16>), dim3(nb), dim3(256), 0, s, g);   \
+  else hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, R16>), dim3(nb), dim3(256), 0, s, g)
   switch (nwl.r_pad / 16) {
     case 0: SVDQ_QLAUNCH(0); break;
     case 2: SVDQ_QLAUNCH(2); break;
@@ -1310,7 +1327,7 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
 #undef SVDQ_QLAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nwl.r_pad == 0) return e;
-  return launch_reduce_down(reinterpret_cast<const float*>(nact + nal.part), N / kTileRows, nal.M_pad,
+  return launch_reduce_down(reinterpret_cast<const float*>(nact + nal.part), N / tile_cols, nal.M_pad,
                             int(nwl.r_pad), reinterpret_cast<uint16_t*>(nact + nal.D), s);
 }
 

@@ -35,6 +35,7 @@
 namespace svdq {
 
 constexpr int kTileRows = 256;     // rows of N (weights) and M (activations) are padded to this
+constexpr int kFusedTileCols = 128; // narrowest output tile of a GEMM that quantizes its output
 constexpr int kKStep = 128;        // K per MFMA step
 constexpr int kKSuper = 512;       // K per scale superfragment; K must be a multiple
 constexpr int kRankAlign = 32;     // rank padded to the bf16 MFMA K
@@ -113,8 +114,8 @@ __host__ __device__ inline void act_split(int K, int r_pad, int64_t M_pad, int* 
 // Codes: M_pad x K/2.  Scales: M_pad x scale_row_bytes(fmt, K).  D: M_pad x r_pad x {hi, lo} bf16.
 // part: fp32 partial down projections, P x M_pad x r_pad, for the larger of the two
 // producers: the activation kernel's K splits (when it splits K), and the GEMM of a
-// previous layer that quantizes its output for this layer (one partial per 256
-// columns of that output, K / 256 of them).
+// previous layer that quantizes its output for this layer (one partial per tile
+// column of that output: K / 128 of them with 128-wide tiles, K / 256 with 256-wide).
 __host__ __device__ inline ActLayout act_layout(int fmt, int K, int rank, int64_t M) {
   ActLayout a;
   a.M_pad = round_up(M > 0 ? M : 1, kTileRows);
@@ -124,7 +125,7 @@ __host__ __device__ inline ActLayout act_layout(int fmt, int K, int rank, int64_
   a.codes = o;  o = align256(o + size_t(a.M_pad) * K / 2);
   a.scales = o; o = align256(o + size_t(a.M_pad) * scale_row_bytes(fmt, K));
   a.D = o;      o = align256(o + size_t(a.M_pad) * a.r_pad * 4);
-  const int nparts = (a.splits > 1 && a.splits > K / kTileRows) ? a.splits : K / kTileRows;
+  const int nparts = (a.splits > 1 && a.splits > K / kFusedTileCols) ? a.splits : K / kFusedTileCols;
   a.part = o;   o = align256(o + size_t(nparts) * a.M_pad * a.r_pad * 4);
   a.total = o;
   return a;
