@@ -59,7 +59,8 @@ template <int WN>
 constexpr int stage_row_bytes() { return WN * 32 + 16; }
 
 // acc += (X_hat L1) L2 over the wave tile: bf16 MFMAs of L2 (A) against D hi and lo (B).
-template <int WN, int WM>
+// ROWCHECK (short tiles only): skip the blocks past the padded rows.
+template <int WN, int WM, bool ROWCHECK = false>
 __device__ __forceinline__ void add_lowrank(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0,
                                             int lane) {
   if (!(g.epi & SVDQ_EPI_LOWRANK) || g.r_pad == 0) return;
@@ -73,7 +74,7 @@ __device__ __forceinline__ void add_lowrank(const GemmArgs& g, v4f (&acc)[WN][WM
     for (int i = 0; i < WN; ++i) l2[i] = L2f[(i * R32 + r32) * 64];
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
-      if (j >= jend) break;
+      if (ROWCHECK && j >= jend) break;
       const uint4 dh = Df[(j * R32 + r32) * 128];
       const uint4 dl = Df[(j * R32 + r32) * 128 + 64];
 #pragma unroll
@@ -429,10 +430,10 @@ __device__ __forceinline__ void store_qkv(const GemmArgs& g, v4f (&acc)[WN][WM],
 // come before any store), then every bias value, then bias + activation +
 // conversion + stores with no loads in between (the vector-memory counter also
 // counts stores, so a load waited on among the stores would wait for them).
-template <int WN, int WM, bool OUT_F32, bool GELU>
+template <int WN, int WM, bool OUT_F32, bool GELU, bool ROWCHECK = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane,
                                          uint8_t* stage) {
-  add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+  add_lowrank<WN, WM, ROWCHECK>(g, acc, n0, m0, lane);
   float bv[WN][4];
   load_bias<WN>(g, n0, lane, bv);
   store_out<WN, WM, OUT_F32, GELU, true>(g, acc, bv, n0, m0, lane, stage);
@@ -668,7 +669,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     load_bias<WN>(g, n0, lane, bv);
     store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
-    epilogue<WN, WMA, OUT_F32, GELU>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+    epilogue<WN, WMA, OUT_F32, GELU, (WMA < WM)>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
 }
 
