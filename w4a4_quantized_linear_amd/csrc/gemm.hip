@@ -101,8 +101,8 @@ __device__ __forceinline__ void load_bias(const GemmArgs& g, int64_t n0, int lan
 
 // Y = act(acc (+ bias)) for the wave tile.  fp32 output: one 16-byte store per
 // lane and block.  bf16 output: each pair of 16-row blocks (the last block alone
-// when their number is odd) goes through the wave's LDS staging area so that every store instruction writes whole
-// 256-byte row segments.
+// when their number is odd) goes through the wave's LDS staging area, so that
+// every store instruction writes whole 256-byte row segments.
 template <int WN, int WM, bool OUT_F32, bool GELU, bool ADD_BIAS>
 __device__ __forceinline__ void store_out(const GemmArgs& g, v4f (&acc)[WN][WM], const float (&bv)[WN][4],
                                           int64_t n0, int64_t m0, int lane, uint8_t* stage) {
@@ -322,9 +322,9 @@ __device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, 
   for (int t = 0; t < WN / 2; ++t)
 #pragma unroll
     for (int s = 0; s < WN / 2; ++s)
-      oor = oor ||
-            exp_out_of_range(*reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + c * 8)),
-                             *reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + 32 + c * 8)));
+      oor = oor || exp_out_of_range(
+                       *reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + c * 8)),
+                       *reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + 32 + c * 8)));
   const bool fast = (wf & (kLamRangeBit | kDivSlowBit)) == 0 && !__any(oor);
   if (__builtin_expect(fast, 1))
     quant_rows<WN, R16, true>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
@@ -1199,6 +1199,19 @@ static int short_tile_blocks(int64_t tiles_n, int64_t M_pad) {
   return best;
 }
 
+// The 256-wide kernel with WMA activation blocks per wave.
+template <int WMA>
+static void launch_big(bool f32, bool gelu, unsigned nb, hipStream_t s, const GemmArgs& g) {
+  if (f32 && gelu)
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g);
+  else if (f32)
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g);
+  else if (gelu)
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g);
+}
+
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s) {
   GemmArgs g{};
@@ -1236,17 +1249,9 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     if (use_big_tiles(big)) {
       const int wma = short_tile_blocks(wl.N_pad / 256, al.M_pad);
       const unsigned nb = unsigned((wl.N_pad / 256) * ((al.M_pad + 32 * wma - 1) / (32 * wma)));
-#define SVDQ_SHORT(WMA)                                                                                          \
-  do {                                                                                                           \
-    if (f32 && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
-    else if (f32) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, true, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
-    else if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
-    else hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, false, WMA>), dim3(nb), dim3(256), 0, s, g); \
-  } while (0)
-      if (wma == 8) SVDQ_SHORT(8);
-      else if (wma == 7) SVDQ_SHORT(7);
-      else SVDQ_SHORT(6);
-#undef SVDQ_SHORT
+      if (wma == 8) launch_big<8>(f32, gelu, nb, s, g);
+      else if (wma == 7) launch_big<7>(f32, gelu, nb, s, g);
+      else launch_big<6>(f32, gelu, nb, s, g);
     } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
     }
