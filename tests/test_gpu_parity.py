@@ -48,6 +48,25 @@ MEDIUM = [
 ]
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes on top of the hand-picked ones: every format, M from
+    1 to 900, K a multiple of 512 up to 2048, N a multiple of 16 up to 1600, ranks
+    0 to 128 including ones that are not multiples of 16."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = ("mxfp4", "int4", "nvfp4")[i % 3]
+        M = int(rng.integers(1, 901))
+        K = 512 * int(rng.integers(1, 5))
+        N = 16 * int(rng.integers(1, 101))
+        rank = int(rng.choice([0, 8, 16, 24, 32, 40, 64, 100, 128]))
+        out.append(("qkv", fmt, M, K, N, rank, 100 + i))
+    return out
+
+
+MEDIUM += _random_cases(12, 2026)
+
+
 def _medium_layer(name, fmt, M, K, N, rank, seed, edge=False):
     spec = synth.layer_spec(name, M=M, K=K, N=N, rank=rank, fmt=fmt, x_outliers=max(1, K // 100),
                             w_outliers=max(1, K // 100), lora_rank=0)
