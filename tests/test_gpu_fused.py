@@ -35,6 +35,22 @@ CASES = [
 ]
 
 
+def _random_cases(n, seed):
+    """Seeded random pairs: M from 1 to 900, K1 a multiple of 512 up to 2048, N1
+    (the next layer's K) a multiple of 512 up to 2048, N2 a multiple of 16 up to
+    1200, ranks 0 to 64 (the next layer's at most 64) not all aligned to 16."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((int(rng.integers(1, 901)), 512 * int(rng.integers(1, 5)), 512 * int(rng.integers(1, 5)),
+                    int(rng.choice([0, 8, 32, 40, 64])), 16 * int(rng.integers(1, 76)),
+                    int(rng.choice([0, 16, 24, 48, 64])), 200 + i))
+    return out
+
+
+CASES += _random_cases(4, 2027)
+
+
 @pytest.fixture(scope="module")
 def torch_dev():
     torch = pytest.importorskip("torch")
