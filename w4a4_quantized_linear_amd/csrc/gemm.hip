@@ -427,13 +427,14 @@ __device__ __forceinline__ void store_qkv(const GemmArgs& g, v4f (&acc)[WN][WM],
 }
 
 // Whole epilogue after the main loop: low-rank MFMAs first (their operand loads
-// come before any store), then every bias value, then bias + activation +
-// conversion + stores with no loads in between (the vector-memory counter also
-// counts stores, so a load waited on among the stores would wait for them).
-template <int WN, int WM, bool OUT_F32, bool GELU, bool ROWCHECK = false>
+// come before any store; LOWRANK false when the kernel started from them), then
+// every bias value, then bias + activation + conversion + stores with no loads
+// in between (the vector-memory counter also counts stores, so a load waited on
+// among the stores would wait for them).
+template <int WN, int WM, bool OUT_F32, bool GELU, bool LOWRANK = true, bool ROWCHECK = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], int64_t n0, int64_t m0, int lane,
                                          uint8_t* stage) {
-  add_lowrank<WN, WM, ROWCHECK>(g, acc, n0, m0, lane);
+  if (LOWRANK) add_lowrank<WN, WM, ROWCHECK>(g, acc, n0, m0, lane);
   float bv[WN][4];
   load_bias<WN>(g, n0, lane, bv);
   store_out<WN, WM, OUT_F32, GELU, true>(g, acc, bv, n0, m0, lane, stage);
@@ -561,19 +562,58 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
   auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WMA + j) * 64 + lane]; };
 
-  // Prologue: scales of superfragment 0, then stages 0..2 into slots 0..2.
+  // Prologue.  128 x 128 tiles: the accumulators start from the low-rank term
+  // (X_hat L1) L2 (bf16 MFMAs of L2 against D hi and lo).  The operands of its
+  // first 32 ranks are loaded ahead of the scales of superfragment 0 and of
+  // stages 0..2 (into slots 0..2), and its MFMAs run while those land; further
+  // 32-rank chunks follow in order.  256-wide tiles (no registers to spare
+  // here) add the low-rank term after the main loop instead.
+  constexpr bool LR_FIRST = WN == 4;
   v4f acc[WN][WMA];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
     for (int j = 0; j < WMA; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  load_scales(sa, sb, 0);
+  const bool lowrank = LR_FIRST && (g.epi & SVDQ_EPI_LOWRANK) && g.r_pad > 0;
+  const int R32 = g.r_pad / 32;
+  const uint4* const L2f = reinterpret_cast<const uint4*>(g.wblob + g.w_L2) + (n0 / 16) * R32 * 64 + lane;
+  const uint4* const Df = reinterpret_cast<const uint4*>(g.act + g.a_D) + (m0 / 16) * R32 * 128 + lane;
+  auto lowrank_operands = [&](int r32, uint4 (&l2)[WN], uint4 (&dh)[WMA], uint4 (&dl)[WMA]) {
 #pragma unroll
-  for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
+    for (int i = 0; i < WN; ++i) l2[i] = L2f[(i * R32 + r32) * 64];
 #pragma unroll
-  for (int f = 0; f < 2 * PW; ++f) fetch1(ring1, 1, f);
+    for (int j = 0; j < WMA; ++j) {
+      dh[j] = Df[(j * R32 + r32) * 128];
+      dl[j] = Df[(j * R32 + r32) * 128 + 64];
+    }
+  };
+  auto lowrank_mfma = [&](const uint4 (&l2)[WN], const uint4 (&dh)[WMA], const uint4 (&dl)[WMA]) {
 #pragma unroll
-  for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+    for (int j = 0; j < WMA; ++j)
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        acc[i][j] = mfma_bf16(l2[i], dh[j], acc[i][j]);
+        acc[i][j] = mfma_bf16(l2[i], dl[j], acc[i][j]);
+      }
+  };
+  {
+    uint4 l2[WN], dh[WMA], dl[WMA];
+    if (lowrank) lowrank_operands(0, l2, dh, dl);
+    load_scales(sa, sb, 0);
+#pragma unroll
+    for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
+#pragma unroll
+    for (int f = 0; f < 2 * PW; ++f) fetch1(ring1, 1, f);
+#pragma unroll
+    for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+    if (lowrank) {
+      lowrank_mfma(l2, dh, dl);
+      for (int r32 = 1; r32 < R32; ++r32) {
+        lowrank_operands(r32, l2, dh, dl);
+        lowrank_mfma(l2, dh, dl);
+      }
+    }
+  }
   wait_barrier<2 * PW>();                          // stages 0 and 1 are in LDS
   // Fragments in registers, reloaded in place.  A step runs its 8 x 8 MFMAs in
   // two halves by activation fragment: half 0 uses fb[0..3] and meanwhile reads
@@ -652,7 +692,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
       lamv[BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlam)[kn];
       lamv[2 * BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlo)[kn];
     }
-    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    if (!LR_FIRST) add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
     uint4 l1r[WN][QOUT > 0 ? QOUT : 1];
@@ -664,12 +704,12 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     quant_h<WN, QOUT>(g, reinterpret_cast<const uint8_t*>(slot(prow >> 6)), prow & 63, lamv, lane, mt0 * 16 + prow,
                       int(nt0 * 16), tn, l1r);
   } else if constexpr (QKV) {
-    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    if (!LR_FIRST) add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
     store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
-    epilogue<WN, WMA, OUT_F32, GELU, (WMA < WM)>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+    epilogue<WN, WMA, OUT_F32, GELU, !LR_FIRST, (WMA < WM)>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
   }
 }
 
