@@ -69,14 +69,14 @@ def _pair(M, K1, N1, r1, N2, r2, seed):
     return synth.draw_layer(s1, seed=seed), synth.draw_layer(s2, seed=seed + 100)
 
 
-def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2):
+def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, epi1=EPI1):
     l1, l2 = sq.Layer("mxfp4", K1, N1, r1), sq.Layer("mxfp4", N1, N2, r2)
     w1, w2 = pack(l1, L1, torch, dev), pack(l2, L2, torch, dev)
     a1 = sq.quantize_act(l1, w1, dev_tensor(L1["X"], torch, dev))
-    print(f"fused pair M={M} {K1}->{N1}->{N2} ranks {r1}/{r2}", flush=True)
-    H = sq.gemm(l1, w1, a1, M, EPI1)
+    print(f"fused pair M={M} {K1}->{N1}->{N2} ranks {r1}/{r2} epi {epi1}", flush=True)
+    H = sq.gemm(l1, w1, a1, M, epi1)
     a2u = sq.quantize_act(l2, w2, H.view(torch.int16))
-    a2f = sq.gemm_quant(l1, w1, a1, M, EPI1, l2, w2)
+    a2f = sq.gemm_quant(l1, w1, a1, M, epi1, l2, w2)
     uu, uf = sq.unpack_act(l2, a2u, M), sq.unpack_act(l2, a2f, M)
     Y2u = sq.gemm(l2, w2, a2u, M, EPI2)
     Y2f = sq.gemm(l2, w2, a2f, M, EPI2)
@@ -113,6 +113,17 @@ def test_fused_equals_unfused_and_oracle_chain(torch_dev, case):
     Y1_o = Ly.forward(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"], "mxfp4", gelu_act=True)["Y"]
     Y2_o = Ly.forward(F.bf16_bits(Y1_o), L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], "mxfp4")["Y"]
     check_chain_output(r["Y2f"].cpu().numpy(), Y2_o, "fused MLP output")
+
+
+@pytest.mark.parametrize("case", [(300, 1024, 1024, 16, 512, 32, 11), (2048, 512, 4608, 32, 256, 16, 12)],
+                         ids=["128x128-tiles", "256x256-tiles"])
+def test_fused_without_gelu(torch_dev, case):
+    """The fused step with the bias and low-rank term but no activation: the
+    codes and scales still equal quantize_act's of the stored output."""
+    torch, dev = torch_dev
+    L1, L2 = _pair(*case)
+    r = _run(torch, dev, L1, L2, *case[:6], epi1=sq.EPI_LOWRANK | sq.EPI_BIAS)
+    _check_against_unfused(torch, r, L2, case[5], f"no GELU, case {case}")
 
 
 def test_fused_ieee_division_path(torch_dev):
