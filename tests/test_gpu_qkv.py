@@ -44,10 +44,21 @@ def _oracle(Y_o, E):
                             E["cos"], E["sin"])
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: M from 1 to 1200, K a multiple of 512 up to 2048,
+    1 to 12 heads per projection, ranks 0 to 64 not all aligned to 16."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 1201)), 512 * int(rng.integers(1, 5)), 3 * 128 * int(rng.integers(1, 13)),
+             int(rng.choice([0, 8, 16, 40, 64])), 300 + i) for i in range(n)]
+
+
 # 128 x 128 tiles (a head split between two waves) in the first three; 256 x 256
-# tiles (192 of them, a head per wave) in the last
-@pytest.mark.parametrize("M,K,N,rank,seed", [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3),
-                                             (2048, 512, 6144, 16, 4)])
+# tiles (192 of them, a head per wave) in the fourth; then seeded random shapes
+QKV_CASES = [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3),
+             (2048, 512, 6144, 16, 4)] + _random_cases(4, 2028)
+
+
+@pytest.mark.parametrize("M,K,N,rank,seed", QKV_CASES)
 def test_qkv_elementwise(torch_dev, M, K, N, rank, seed):
     torch, dev = torch_dev
     spec = synth.layer_spec("qkv", M=M, K=K, N=N, rank=rank, x_outliers=max(1, K // 100),
