@@ -42,6 +42,17 @@ CASES = [
 ]
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes: M from 1 to 64 (both the LDS and the direct path),
+    K a multiple of 512 up to 4096, N a multiple of 16 up to 8192."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 65)), 512 * int(rng.integers(1, 9)), 16 * int(rng.integers(1, 513)), 400 + i)
+            for i in range(n)]
+
+
+CASES += _random_cases(4, 2029)
+
+
 @pytest.fixture(scope="module")
 def torch_dev():
     torch = pytest.importorskip("torch")
