@@ -50,7 +50,8 @@
  *
  * Shapes: K % 512 == 0, 16 <= N, N % 16 == 0, 0 <= rank <= 256, M >= 0,
  * K <= 65536, N <= 65536.  Row strides (ldx, ldy) are in elements and
- * multiples of 8 (16-byte rows).  Device buffers must be 16-byte aligned;
+ * multiples of 8 (16-byte rows); ldx <= 2^24 (the kernels address 16 rows of X
+ * with 32-bit offsets), else SVDQ_ERR_SHAPE.  Device buffers must be 16-byte aligned;
  * packed weights and activation workspaces 256-byte aligned.
  */
 #ifndef SVDQ_H

@@ -8,6 +8,7 @@ returns; neither is imported here.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
+    SEEDS,
     LayerSpec,
     bf16_bits_from_f32,
     bf16_bits_to_f32,

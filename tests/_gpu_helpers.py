@@ -90,3 +90,21 @@ def check_chain_output(Y, Y_o, what):
     assert mean_rel <= Ly.MEAN_REL and frac <= 1e-3 and err.max() <= 0.25 * rms, \
         f"{what}: mean rel {mean_rel:.2e}, fraction over 2e-2 rms {frac:.2e}, max/rms {err.max() / rms:.3f}"
     return mean_rel, frac
+
+
+def check_next_layer_on_gpu_h(torch, ua, L2, H, Y2f, fmt, rows, what):
+    """The oracle's next layer on the GPU's own bf16 H (its rows `rows`): `ua`
+    (the GPU's unpacked activation workspace of that layer for H) must hold the
+    oracle's codes and scales of H_hat bit for bit, and a down projection within
+    the bound of a bf16 hi + lo split summed in fp32; the layer's fp32 output
+    Y2f must meet the full tolerance against the oracle's on the same H."""
+    Hb = H.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    ref = Ly.forward(Hb, L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], fmt)
+    assert_codes_equal(ua["codes"].cpu().numpy()[rows], ref["cX"], f"{what}: codes of H_hat")
+    assert_scales_equal(scales_np(ua["scales"], fmt)[rows], ref["sX"], f"{what}: scales of H_hat")
+    if np.asarray(L2["L1"]).shape[1]:
+        Dg = ua["D"].cpu().numpy()[rows].astype(np.float64)
+        bound = np.abs(ref["xhat"].astype(np.float64)) @ np.abs(F.bf16_value(L2["L1"]))
+        assert np.all(np.abs(Dg - ref["D"]) <= 2.0 ** -14 * bound + 1e-30), f"{what}: down projection"
+    check_fp32_output(Y2f.cpu().numpy()[rows], ref["Y"], f"{what}: output")
+    return ref

@@ -100,6 +100,8 @@ def test_quantize_act_validation(L, forced_device_error):
     assert f(d, P, P, -1, 1024, P, None) == 2
     assert f(d, P, P, 4, 1000, P, None) == 2          # ldx < K
     assert f(d, P, P, 4, 1028, P, None) == 4          # ldx not a multiple of 8
+    assert f(d, P, P, 4, (1 << 24) + 8, P, None) == 2  # ldx beyond 2^24 (32-bit row offsets)
+    assert f(d, P, P, 4, 1 << 24, P, None) == 6
     assert f(d, P, P + 2, 4, 1024, P, None) == 4
     assert f(ctypes.byref(D(fmt=9)), P, P, 4, 1024, P, None) == 3
     assert f(d, P, P, 4, 1024, P, None) == 6
@@ -117,6 +119,7 @@ def test_gemm_and_linear_validation(L, forced_device_error):
     assert lin(d, P, P, 4, 1024, P, 512, 3, P, need - 1, None) == 5
     assert lin(d, P, P, 4, 1024, P, 512, 3, P, need, None) == 6
     assert lin(d, P, P, 4, 1024, P, 512, 3, None, need, None) == 1
+    assert lin(d, P, P, 4, (1 << 24) + 8, P, 512, 3, P, need, None) == 2
 
 
 def test_gemm_quant_validation(L, forced_device_error):

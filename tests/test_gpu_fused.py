@@ -1,21 +1,26 @@
 """Fused MLP step (svdq_gemm_quant): the first layer's GEMM quantizes its bf16
 output H for the next layer instead of storing it.
 
-Checked against the unfused path on the same GPU inputs: svdq_gemm writes H,
-svdq_quantize_act quantizes it, and the fused call must leave the next layer's
-workspace with the same codes and scales bit for bit, and a down projection
-within the rounding bound of two fp32 sums of the same bf16 products.  Through
-the next layer's GEMM the fused chain is also checked against the oracle's
-chain (each side quantizes its own H), as the unfused chain is."""
+The unfused path on the same GPU inputs writes H (svdq_gemm).  That H is
+checked against the oracle's first layer, then handed to the oracle's next
+layer: the fused workspace (and the unfused svdq_quantize_act of H) must hold
+the oracle's codes and scales of H_hat bit for bit and a down projection within
+the hi + lo rounding bound, and the next layer's output from either workspace
+must meet the full tolerance against the oracle's on that H.  The fused and
+unfused workspaces are also compared with each other (same codes and scales,
+D within the bound of two fp32 sums of the same products), and the chain with
+each side feeding its own H is checked under the looser chain bound."""
 import numpy as np
 import pytest
 
+import _calib
 import synth
 import w4a4_quantized_linear_amd as sq
 from oracle import formats as F
 from oracle import layer as Ly
 
-from _gpu_helpers import bf16_to_np, check_chain_output, dev_tensor, pack
+from _gpu_helpers import (bf16_to_np, check_bf16_output, check_chain_output, check_next_layer_on_gpu_h,
+                          dev_tensor, pack)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +89,20 @@ def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, epi1=EPI1):
     return dict(H=H, uu=uu, uf=uf, Y2u=Y2u, Y2f=Y2f)
 
 
+def _check_against_oracle(torch, r, L1, L2, M, what, rows=None, epi1=EPI1):
+    """The GPU's H against the oracle's first layer, then the oracle's next layer
+    on that H against both workspaces and both outputs: the second layer is
+    judged on the input it actually received."""
+    rows = np.arange(M) if rows is None else rows
+    gelu = (epi1 & sq.EPI_GELU) != 0
+    Y1_o = Ly.forward_rows(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"] if epi1 & sq.EPI_BIAS else None,
+                           "mxfp4", rows, gelu_act=gelu)
+    check_bf16_output(bf16_to_np(r["H"])[rows], Y1_o, f"{what}: first layer's H")
+    ref = check_next_layer_on_gpu_h(torch, r["uf"], L2, r["H"], r["Y2f"], "mxfp4", rows, f"{what}: fused")
+    check_next_layer_on_gpu_h(torch, r["uu"], L2, r["H"], r["Y2u"], "mxfp4", rows, f"{what}: unfused")
+    return ref
+
+
 def _check_against_unfused(torch, r, L2, r2, what):
     uu, uf = r["uu"], r["uf"]
     assert torch.equal(uu["codes"], uf["codes"]), f"{what}: codes differ from quantize_act(H)"
@@ -108,6 +127,7 @@ def test_fused_equals_unfused_and_oracle_chain(torch_dev, case):
     M, K1, N1, r1, N2, r2, seed = case
     L1, L2 = _pair(*case)
     r = _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2)
+    _check_against_oracle(torch, r, L1, L2, M, f"case {case}")
     _check_against_unfused(torch, r, L2, r2, f"case {case}")
     # the chain through the oracle, which forms and quantizes its own H
     Y1_o = Ly.forward(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"], "mxfp4", gelu_act=True)["Y"]
@@ -122,7 +142,9 @@ def test_fused_without_gelu(torch_dev, case):
     codes and scales still equal quantize_act's of the stored output."""
     torch, dev = torch_dev
     L1, L2 = _pair(*case)
-    r = _run(torch, dev, L1, L2, *case[:6], epi1=sq.EPI_LOWRANK | sq.EPI_BIAS)
+    epi1 = sq.EPI_LOWRANK | sq.EPI_BIAS
+    r = _run(torch, dev, L1, L2, *case[:6], epi1=epi1)
+    _check_against_oracle(torch, r, L1, L2, case[0], f"no GELU, case {case}", epi1=epi1)
     _check_against_unfused(torch, r, L2, case[5], f"no GELU, case {case}")
 
 
@@ -137,15 +159,27 @@ def test_fused_ieee_division_path(torch_dev):
     lam[700] = np.float32(2.0 ** -35)
     L2["lam"] = lam
     r = _run(torch, dev, L1, L2, *case[:6])
+    _check_against_oracle(torch, r, L1, L2, case[0], "lambda outside the fast range")
     _check_against_unfused(torch, r, L2, case[5], "lambda outside the fast range")
 
 
-def test_fused_full_size_flux_mlp(torch_dev):
+@pytest.mark.parametrize("kind", ["calibrated", "drawn"])
+def test_fused_full_size_flux_mlp(torch_dev, kind):
     """The FLUX MLP pair at its real size (fc1 4608 x 3072 -> 12288, GELU; fc2
-    12288 -> 3072; rank 32), as the benchmark's fused step runs it: codes and
-    scales of every row equal quantize_act's, D and fc2's output within bounds."""
+    12288 -> 3072; rank 32), as the benchmark's fused step runs it, on the
+    calibrated operands and on drawn ones: on sampled rows, H against the
+    oracle's fc1 and the fused workspace and fc2's output against the oracle's
+    fc2 on the GPU's H; on every row, codes and scales equal quantize_act's and
+    D and fc2's output lie within bounds of the unfused path."""
     torch, dev = torch_dev
     s1, s2 = synth.CONFIGS["fc1_mxfp4"], synth.CONFIGS["fc2_mxfp4"]
-    L1, L2 = synth.draw_layer(s1), synth.draw_layer(s2)
+    print(f"fused FLUX MLP pair, {kind} operands", flush=True)
+    if kind == "calibrated":
+        L1, L2 = _calib.calibrated_layer(s1), _calib.calibrated_layer(s2)
+    else:
+        L1, L2 = synth.draw_layer(s1), synth.draw_layer(s2)
     r = _run(torch, dev, L1, L2, s1.M, s1.K, s1.N, s1.rank, s2.N, s2.rank)
-    _check_against_unfused(torch, r, L2, s2.rank, "FLUX MLP pair")
+    rng = np.random.default_rng(78)
+    rows = np.unique(np.concatenate([[0, s1.M - 1], rng.choice(s1.M, 30, replace=False)]))
+    _check_against_oracle(torch, r, L1, L2, s1.M, f"FLUX MLP pair ({kind})", rows=rows)
+    _check_against_unfused(torch, r, L2, s2.rank, f"FLUX MLP pair ({kind})")

@@ -47,10 +47,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build(verbose: bool = True) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,6 +56,20 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile each source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    cflags = [f for f in flags() if f != "-shared"]
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        list(ex.map(lambda so: _run([hipcc()] + cflags + ["-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fno-gpu-rdc"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     with open(LIB + ".srchash", "w") as f:
         f.write(source_hash())

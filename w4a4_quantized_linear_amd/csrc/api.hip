@@ -43,7 +43,7 @@ namespace {
 constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int kGemmQuantMaxRank = 64;   // next layer's rank in svdq_gemm_quant (4 rank tiles of 16)
 constexpr int kQkvHeadDim = 128;        // svdq_gemm_qkv: one head per 128 output columns of a wave
-constexpr int64_t kW4A16MaxLdx = int64_t(1) << 24;   // svdq_gemm_w4a16: 16 rows of X within a 32-bit buffer range
+constexpr int64_t kMaxLdx = int64_t(1) << 24;   // 16 rows of X within a kernel's 32-bit buffer range
 constexpr uint32_t kEpiAll = SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU | SVDQ_EPI_OUT_F32;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -86,7 +86,7 @@ svdq_status check_act_args(const svdq_layer_desc* d, const void* w_packed, const
   if (!d || !w_packed || !a_packed || (M > 0 && !X)) return SVDQ_ERR_NULL;
   svdq_status s = check_shape(d);
   if (s != SVDQ_OK) return s;
-  if (M < 0 || M > kMaxRows || ldx < d->K) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > kMaxRows || ldx < d->K || ldx > kMaxLdx) return SVDQ_ERR_SHAPE;
   if ((s = check_fmt(d)) != SVDQ_OK) return s;
   if (!aligned(w_packed, 256) || !aligned(a_packed, 256) || (M > 0 && !aligned(X, 16)) || ldx % 8 != 0)
     return SVDQ_ERR_ALIGN;
@@ -245,7 +245,7 @@ svdq_status svdq_gemm_w4a16(const svdq_layer_desc* d, const void* w_packed, cons
   if (!d || !w_packed || (M > 0 && (!X || !Y))) return SVDQ_ERR_NULL;
   svdq_status s = check_shape(d);
   if (s != SVDQ_OK) return s;
-  if (M < 0 || M > kMaxRows || ldx < d->K || ldx > kW4A16MaxLdx || ldy < d->N) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > kMaxRows || ldx < d->K || ldx > kMaxLdx || ldy < d->N) return SVDQ_ERR_SHAPE;
   if ((s = check_fmt(d)) != SVDQ_OK) return s;
   if (d->fmt != SVDQ_INT4_G64 || d->rank != 0 || (epi & ~(SVDQ_EPI_BIAS | SVDQ_EPI_OUT_F32)) != 0)
     return SVDQ_ERR_FORMAT;
