@@ -72,7 +72,8 @@ typedef enum {
   SVDQ_ERR_ALIGN = 4,     /* a pointer or stride is not aligned as required      */
   SVDQ_ERR_WORKSPACE = 5, /* workspace smaller than svdq_act_bytes               */
   SVDQ_ERR_DEVICE = 6,    /* no device, or the current device is not gfx950      */
-  SVDQ_ERR_LAUNCH = 7     /* a kernel launch failed                              */
+  SVDQ_ERR_LAUNCH = 7,    /* a kernel launch failed                              */
+  SVDQ_ERR_TOO_LARGE = 8  /* svdq_linear_noalloc: the layer's workspace exceeds its static scratch */
 } svdq_status;
 
 typedef enum {
@@ -198,6 +199,22 @@ svdq_status svdq_gemm_w4a16(const svdq_layer_desc* d, const void* w_packed, cons
 svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
                         int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* svdq_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments as svdq_linear minus the workspace, same kernels and the same
+ * result bits; the activation workspace instead lives in a static device array
+ * of 64 MiB inside the library (one per GPU, allocated with the library's code
+ * on that GPU and held until the process ends; no call allocates or frees
+ * anything).  A layer whose workspace (codes, scales, the down projection and
+ * its K-split partials: about M (K/2 + K/32 + 4 r) bytes plus the partials)
+ * exceeds 64 MiB gives SVDQ_ERR_TOO_LARGE before anything is enqueued; the FLUX
+ * shapes need at most 38 MiB (M = 4608, K = 12288).  Every call on a GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialized by the caller.  Each call
+ * overwrites every byte it reads, so the previous call's contents never matter. */
+svdq_status svdq_linear_noalloc(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X,
+                                int64_t M, int64_t ldx, void* Y, int64_t ldy, uint32_t epi, void* stream);
 
 /* Test access to the opaque layouts, in canonical form (device outputs, any may be NULL):
  *   codes   uint8 rows x K/2: two 4-bit codes per byte, element 2j in the low nibble

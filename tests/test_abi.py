@@ -43,8 +43,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 104
-    for s in range(8):
+    assert L.svdq_version() == 105
+    for s in range(9):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
 
@@ -120,6 +120,24 @@ def test_gemm_and_linear_validation(L, forced_device_error):
     assert lin(d, P, P, 4, 1024, P, 512, 3, P, need, None) == 6
     assert lin(d, P, P, 4, 1024, P, 512, 3, None, need, None) == 1
     assert lin(d, P, P, 4, (1 << 24) + 8, P, 512, 3, P, need, None) == 2
+
+
+def test_linear_noalloc_validation(L, forced_device_error):
+    f = L.svdq_linear_noalloc
+    d = ctypes.byref(D())
+    assert f(d, P, P, 4, 1024, P, 512, 3, None) == 6                  # valid -> device check
+    assert f(d, P, None, 0, 1024, None, 512, 3, None) == 6            # M = 0: X and Y may be NULL
+    assert f(None, P, P, 4, 1024, P, 512, 3, None) == 1
+    assert f(d, None, P, 4, 1024, P, 512, 3, None) == 1
+    assert f(d, P, P, 4, 1024, None, 512, 3, None) == 1
+    assert f(d, P, P, 4, 1000, P, 512, 3, None) == 2                  # ldx < K
+    assert f(d, P, P, 4, 1024, P, 500, 3, None) == 2                  # ldy < N
+    assert f(d, P, P, 4, 1024, P, 512, 16, None) == 3                 # unknown flag
+    assert f(d, P + 64, P, 4, 1024, P, 512, 3, None) == 4             # blob 256-aligned
+    # the workspace of the FLUX shapes fits the 64 MiB scratch; a larger one is refused
+    assert f(ctypes.byref(D(K=12288, N=3072, rank=32)), P, P, 4608, 12288, P, 3072, 3, None) == 6
+    assert f(ctypes.byref(D(K=65536, N=512, rank=16)), P, P, 4096, 65536, P, 512, 3, None) == 8
+    assert b"64 MiB" in L.svdq_status_str(8)
 
 
 def test_gemm_quant_validation(L, forced_device_error):

@@ -166,6 +166,21 @@ def linear(layer: Layer, w_packed, X, epi: int, out=None, workspace=None, stream
     return out
 
 
+def linear_noalloc(layer: Layer, w_packed, X, epi: int, out=None, stream=None):
+    """svdq_linear with the workspace in the library's static scratch (no device
+    allocation by the library; `out` is allocated here when not given)."""
+    torch = _torch()
+    d, p = _desc_ref(layer)
+    M = X.shape[0]
+    if out is None:
+        dt = torch.float32 if epi & EPI_OUT_F32 else torch.bfloat16
+        out = torch.empty((M, layer.N), dtype=dt, device=X.device)
+    st = lib().svdq_linear_noalloc(p, _ptr(w_packed), _ptr(X), M, X.stride(0), _ptr(out), out.stride(0), epi,
+                                   _stream(stream))
+    check("svdq_linear_noalloc", st)
+    return out
+
+
 def _scales_out(torch, layer: Layer, rows: int, dev):
     """Canonical scales: one byte per group (E8M0 for MXFP4, E4M3 for NVFP4) or fp16 bits (INT4)."""
     dt = torch.int16 if layer.fmt == "int4" else torch.uint8

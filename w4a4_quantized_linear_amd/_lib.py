@@ -15,7 +15,7 @@ EPI_GELU = 4
 EPI_OUT_F32 = 8
 
 STATUS = {0: "SVDQ_OK", 1: "SVDQ_ERR_NULL", 2: "SVDQ_ERR_SHAPE", 3: "SVDQ_ERR_FORMAT", 4: "SVDQ_ERR_ALIGN",
-          5: "SVDQ_ERR_WORKSPACE", 6: "SVDQ_ERR_DEVICE", 7: "SVDQ_ERR_LAUNCH"}
+          5: "SVDQ_ERR_WORKSPACE", 6: "SVDQ_ERR_DEVICE", 7: "SVDQ_ERR_LAUNCH", 8: "SVDQ_ERR_TOO_LARGE"}
 
 # Every function the header declares, with (restype, argtypes).
 _P = ctypes.c_void_p
@@ -32,6 +32,7 @@ SIGNATURES = {
                                      _P, _P, _P, _I64, _P]),
     "svdq_gemm_w4a16": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _I64, ctypes.c_uint32, _P]),
     "svdq_linear": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _I64, ctypes.c_uint32, _P, ctypes.c_size_t, _P]),
+    "svdq_linear_noalloc": (ctypes.c_int, [_D, _P, _P, _I64, _I64, _P, _I64, ctypes.c_uint32, _P]),
     "svdq_unpack_weight": (ctypes.c_int, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "svdq_unpack_act": (ctypes.c_int, [_D, _P, _I64, _P, _P, _P, _P]),
     "svdq_status_str": (ctypes.c_char_p, [ctypes.c_int]),

@@ -38,6 +38,14 @@ hipError_t launch_unpack_act(int fmt, int K, int rank, int64_t M, const ActLayou
 
 using namespace svdq;
 
+// Scratch of svdq_linear_noalloc: the layer's activation workspace (codes,
+// scales, D, K-split partials) in a static device array, one copy per GPU the
+// library runs on, held until the process ends.  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 constexpr int64_t kMaxRows = int64_t(1) << 26;
@@ -81,6 +89,25 @@ svdq_status device_check() {
 
 svdq_status launched(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_LAUNCH; }
 
+// Per-device address of `scratch` (nullptr until the first svdq_linear_noalloc on that device).
+std::atomic<uint8_t*> g_scratch_addr[64];
+
+// Device address of this device's scratch array, looked up on the first call
+// per device (SVDQ_ERR_DEVICE if the lookup fails).
+svdq_status scratch_address(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SVDQ_ERR_DEVICE;
+  uint8_t* p = g_scratch_addr[dev].load();
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return SVDQ_ERR_DEVICE;
+    p = static_cast<uint8_t*>(q);
+    g_scratch_addr[dev].store(p);
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+
 svdq_status check_act_args(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M, int64_t ldx,
                            const void* a_packed) {
   if (!d || !w_packed || !a_packed || (M > 0 && !X)) return SVDQ_ERR_NULL;
@@ -110,7 +137,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 104; }
+int svdq_version(void) { return 105; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -122,6 +149,7 @@ const char* svdq_status_str(svdq_status s) {
     case SVDQ_ERR_WORKSPACE: return "workspace smaller than svdq_act_bytes";
     case SVDQ_ERR_DEVICE: return "no device, or the current device is not gfx950 (MI355X)";
     case SVDQ_ERR_LAUNCH: return "kernel launch failed";
+    case SVDQ_ERR_TOO_LARGE: return "layer needs more than the 64 MiB static scratch of svdq_linear_noalloc";
   }
   return "unknown status";
 }
@@ -268,6 +296,31 @@ svdq_status svdq_linear(const svdq_layer_desc* d, const void* w_packed, const ui
   if (M == 0) return SVDQ_OK;
   if ((s = svdq_quantize_act(d, w_packed, X, M, ldx, workspace, stream)) != SVDQ_OK) return s;
   return svdq_gemm(d, w_packed, workspace, M, Y, ldy, epi, stream);
+}
+
+svdq_status svdq_linear_noalloc(const svdq_layer_desc* d, const void* w_packed, const uint16_t* X, int64_t M,
+                                int64_t ldx, void* Y, int64_t ldy, uint32_t epi, void* stream) {
+  // w_packed stands in for the workspace pointer the checks expect (non-NULL, 256-aligned)
+  svdq_status s = check_act_args(d, w_packed, X, M, ldx, w_packed);
+  if (s != SVDQ_OK) return s;
+  if ((s = check_gemm_args(d, w_packed, w_packed, M, Y, ldy, epi)) != SVDQ_OK) return s;
+  const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
+  if (act_linear_bytes(al) > kScratchBytes) return SVDQ_ERR_TOO_LARGE;
+  if ((s = device_check()) != SVDQ_OK) return s;
+  if (M == 0) return SVDQ_OK;
+  uint8_t* ws = nullptr;
+  if ((s = scratch_address(&ws)) != SVDQ_OK) return s;
+  const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
+  const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_quantize_act(d->fmt, X, M, ldx, d->K, reinterpret_cast<const float*>(blob + wl.lam),
+                                     reinterpret_cast<const float*>(blob + wl.rlam),
+                                     reinterpret_cast<const float*>(blob + wl.rlo), blob + wl.L1, ws + al.codes,
+                                     ws + al.scales, al.M_pad, reinterpret_cast<uint16_t*>(ws + al.D),
+                                     reinterpret_cast<float*>(ws + al.part), int(al.r_pad), al.kr, al.splits,
+                                     reinterpret_cast<const uint32_t*>(blob + wl.flags), st);
+  if (e != hipSuccess) return SVDQ_ERR_LAUNCH;
+  return launched(launch_gemm(d->fmt, blob, wl, ws, al, d->K, d->N, M, Y, ldy, epi, st));
 }
 
 svdq_status svdq_unpack_weight(const svdq_layer_desc* d, const void* w_packed, uint8_t* codes, void* scales,

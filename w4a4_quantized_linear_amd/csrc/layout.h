@@ -131,6 +131,13 @@ __host__ __device__ inline ActLayout act_layout(int fmt, int K, int rank, int64_
   return a;
 }
 
+// Bytes of the workspace that the two launches of one layer touch: codes,
+// scales, D and the activation kernel's K-split partials (without the room a
+// fused producer's partials take).
+__host__ __device__ inline size_t act_linear_bytes(const ActLayout& a) {
+  return a.part + (a.splits > 1 ? size_t(a.splits) * a.M_pad * a.r_pad * 4 : 0);
+}
+
 // ---- codes: byte offset of the 16-byte lane chunk of tile (rt, ks), lane L ----
 __host__ __device__ inline size_t code_chunk(int64_t rt, int ks, int K, int L) {
   return (size_t(rt) * (K / kKStep) + ks) * 1024 + size_t(L) * 16;
