@@ -7,7 +7,10 @@ on synthetic seeded inputs already resident in HBM (weights packed once before
 timing, as at load time).  value = (2 M N K of fc1 + of fc2) per step / time.
 
 Prints one JSON line.  `roofline` is the fc1 GEMM kernel (the dominant launch),
-timed with HIP events around each of its launches inside the timed region.
+timed with HIP events around each of its launches inside the timed region (the
+only markers there); `breakdown` times every launch with events in a second,
+untimed pass.  Before the warmup steps the same steps run untimed for
+--settle-ms so that the shader clock has left its idle level.
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 With --workload mod_w4a16 the step is one W4A16 launch (svdq_gemm_w4a16: bf16
 activations times INT4 weights, the memory-bound modulation projection) and
@@ -16,6 +19,18 @@ launch over its event-timed duration.
 For the MXFP4 pair, `fused_mlp` times the same pair with fc1's GEMM quantizing
 its output for fc2 in its epilogue (svdq_gemm_quant: three launches plus the
 down-projection sum instead of four), same inputs, same step count.
+
+Operands (--operands): "calibrated" (default) converts each workload's dense
+seeded draw the way the SVDQuant notes page, section 4.2, makes a layer
+(smoothing factors from the data, SVD of the smoothed weight, residual), with
+w4a4_quantized_linear_amd.convert on the host before timing; the MLP pair's
+second layer is calibrated on the dense MLP's hidden activation
+GELU(X W1 + b1).  "drawn" takes synth.draw_layer's look-alike operands.
+
+`cold` repeats the timed loop over three or more copies of every operand,
+workspace and output (more bytes than the 256 MB last-level cache), so each
+step reads its operands from HBM; `repeats` gives the median of five more hot
+runs of the same loop; `clock` is what rocm-smi reports before and after.
 """
 from __future__ import annotations
 
@@ -50,6 +65,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE) + list(W4A16))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--operands", default="calibrated", choices=["calibrated", "drawn"],
+                   help="layer operands: converted from the dense draw (default) or drawn look-alikes")
+    p.add_argument("--no-cold", action="store_true", help="skip the cold (operand-rotating) timing")
+    p.add_argument("--settle-ms", type=float, default=300.0,
+                   help="run untimed steps for this long before the warmup, so the shader clock has ramped up")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the timed region, copy MIB mebibytes device to device once (a plain copy of "
                         "known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -87,7 +107,69 @@ def traffic_for(kernel: str, workload: str):
     return None
 
 
-def gpu_leg(args):
+def _bits(t):
+    """uint16 numpy view of a bf16 CPU tensor."""
+    import numpy as np
+    import torch
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def calibrated_operands(spec):
+    """The layer converted from its dense seeded draw (host, float64): smoothing
+    factors from the activations it is calibrated on, SVD of the smoothed
+    weight, bf16 factors, fp32 residual.  The second layer of the MLP pair is
+    calibrated on GELU(X W1 + b1) of the dense first layer (bf16), which is also
+    its input in the CPU baseline.  Cached under $TMPDIR by workload and seed."""
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    import synth
+    from w4a4_quantized_linear_amd import convert
+
+    base = spec.name.split("_")[0] if spec.name.startswith(("fc1_", "fc2_")) else spec.name
+    cdir = os.path.join(tempfile.gettempdir(), "svdq_bench_calib")
+    path = os.path.join(cdir, f"{base}_M{spec.M}_K{spec.K}_N{spec.N}_r{spec.rank}_l{spec.lora_rank}.npz")
+    if os.path.exists(path):
+        try:
+            with np.load(path) as z:
+                return {k: z[k] for k in z.files}
+        except (OSError, ValueError):
+            pass
+    raw = synth.draw_raw(spec)
+    if spec.name.startswith("fc2_"):
+        raw1 = synth.draw_raw(synth.CONFIGS[spec.name.replace("fc2_", "fc1_")])
+        y = _bf16(raw1["X"]).double() @ _bf16(raw1["W"]).double() + _bf16(raw1["b"]).double()
+        X = _bits((0.5 * y * (1.0 + torch.erf(y * 0.7071067811865476))).to(torch.bfloat16))
+        del raw1, y
+    else:
+        X = raw["X"]
+    adapter = (_bf16(raw["A"]), _bf16(raw["B"])) if spec.lora_rank else None
+    c = convert.convert_linear(_bf16(X), _bf16(raw["W"]).t(), spec.rank, _bf16(raw["b"]), adapter)
+    out = {"X": X, "lam": c["lam"].numpy(), "L1": _bits(c["L1"]), "L2": _bits(c["L2"]), "R": c["R"].numpy(),
+           "b": _bits(c["b"])}
+    try:
+        os.makedirs(cdir, exist_ok=True)
+        np.savez(path + ".tmp.npz", **out)
+        os.replace(path + ".tmp.npz", path)
+    except OSError:
+        pass
+    return out
+
+
+def layer_operands(specs, kind):
+    import synth
+    return [calibrated_operands(s) if kind == "calibrated" else synth.draw_layer(s) for s in specs]
+
+
+def gpu_leg(args, ops):
     import numpy as np
     import torch
 
@@ -99,7 +181,7 @@ def gpu_leg(args):
     specs = layers_of(args.workload)
     layers, weights, inputs = [], [], []
     for i, spec in enumerate(specs):
-        L = synth.draw_layer(spec)
+        L = ops[i]
         r = spec.rank + spec.lora_rank
         layer = sq.Layer(spec.fmt, spec.K, spec.N, r)
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
@@ -107,7 +189,6 @@ def gpu_leg(args):
         layers.append(layer)
         weights.append(w)
         inputs.append(t(L["X"]) if i == 0 else None)
-        del L
     M = specs[0].M
     ws = [torch.empty(sq.act_bytes(l, M), dtype=torch.uint8, device=dev) for l in layers]
     outs = [torch.empty((M, l.N), dtype=torch.bfloat16, device=dev) for l in layers]
@@ -116,19 +197,38 @@ def gpu_leg(args):
 
     n = len(layers)
 
-    def step(ev=None):
-        x = inputs[0]
+    # The roofline kernel: the first layer's GEMM (fc1 of the MLP pair, whose
+    # GELU epilogue makes it the longest launch).
+    i_dom = 0
+
+    def step(ev=None, opset=None, dom_ev=None):
+        """One pass of the hot path.  ev: events around every launch; dom_ev: a
+        pair of events around the roofline GEMM only (fewer markers in the
+        timed region)."""
+        wts, x, wss, ots = opset if opset is not None else (weights, inputs[0], ws, outs)
         for i in range(n):
             if ev is not None:
                 ev[i][0].record()
-            sq.quantize_act(layers[i], weights[i], x, out=ws[i])
+            sq.quantize_act(layers[i], wts[i], x, out=wss[i])
             if ev is not None:
                 ev[i][1].record()
-            sq.gemm(layers[i], weights[i], ws[i], M, epis[i], out=outs[i])
+            if dom_ev is not None and i == i_dom:
+                dom_ev[0].record()
+            sq.gemm(layers[i], wts[i], wss[i], M, epis[i], out=ots[i])
+            if dom_ev is not None and i == i_dom:
+                dom_ev[1].record()
             if ev is not None:
                 ev[i][2].record()
-            x = outs[i].view(torch.int16)
+            x = ots[i].view(torch.int16)
 
+    # Clock settling: the shader clock ramps up over the first ~0.1 s of load,
+    # so the same steps run untimed for at least `settle_ms` before the warmup.
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms and settle_steps < 5000:
+        step()
+        settle_steps += 1
+        if settle_steps % 16 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -140,35 +240,40 @@ def gpu_leg(args):
         torch.cuda.synchronize()
         del src, dst
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, events only around the roofline GEMM.
+    dom = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        step(evs[k])
+        step(dom_ev=dom[k])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
-
-    quant_us = [sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) * 1e3 / args.steps
-                for i in range(n)]
-    gemm_us = [sum(evs[k][i][1].elapsed_time(evs[k][i][2]) for k in range(args.steps)) * 1e3 / args.steps
-               for i in range(n)]
+    dom_us = sum(dom[k][0].elapsed_time(dom[k][1]) for k in range(args.steps)) * 1e3 / args.steps
     flops = [2.0 * M * s.N * s.K for s in specs]
     ms_per_step = wall * 1e3 / args.steps
     value = sum(flops) / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the GEMM with the most work (fc1 for the MLP pair)
-    i_dom = max(range(n), key=lambda i: gemm_us[i])
+    # Per-launch breakdown: the same steps again after the timed region, with
+    # events around every launch.
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    quant_us = [sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) * 1e3 / args.steps
+                for i in range(n)]
+    gemm_us = [sum(evs[k][i][1].elapsed_time(evs[k][i][2]) for k in range(args.steps)) * 1e3 / args.steps
+               for i in range(n)]
     fmt = specs[i_dom].fmt
-    achieved = flops[i_dom] / (gemm_us[i_dom] * 1e-6) / 1e12
+    achieved = flops[i_dom] / (dom_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[fmt]
     kname = f"gemm_{fmt}_{specs[i_dom].name}"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(kname, args.workload),
-                "kernel": kname, "flops_per_launch": flops[i_dom], "avg_launch_us": round(gemm_us[i_dom], 2)}
+                "kernel": kname, "flops_per_launch": flops[i_dom], "avg_launch_us": round(dom_us, 2)}
     breakdown = {}
     for i, s in enumerate(specs):
         hbm_q = 2 * M * s.K + M * s.K // 2 + M * s.K // 32 + 4 * M * layers[i].rank + 2 * s.K * layers[i].rank
@@ -179,6 +284,20 @@ def gpu_leg(args):
             "gemm_TFLOPs": round(flops[i] / (gemm_us[i] * 1e-6) / 1e12, 1),
             "linear_TOPS": round(flops[i] / ((gemm_us[i] + quant_us[i]) * 1e-6) / 1e12, 1),
         }
+    repeats = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(args.steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        repeats.append(a.elapsed_time(b) / args.steps)
+    rep = sorted(repeats)
+    repeat_info = {"ms_per_step": [round(x, 4) for x in repeats], "median_ms_per_step": round(rep[2], 4),
+                   "median_value": round(sum(flops) / (rep[2] * 1e-3) / 1e12, 2)}
+    cold = None if args.no_cold else cold_pair(args, torch, step, layers, weights, inputs[0], ws, outs,
+                                                sum(flops), gemm_us, i_dom)
     fused = None
     if args.workload == "mlp_mxfp4":
         fused = fused_pair(args, sq, torch, layers, weights, inputs[0], ws, outs, epis, M, sum(flops))
@@ -186,7 +305,53 @@ def gpu_leg(args):
         fused = fused_qkv(args, sq, synth, torch, np, layers[0], weights[0], inputs[0], ws[0], outs[0], epis[0], M,
                           flops[0])
     return dict(value=value, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps, roofline=roofline,
-                breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused)
+                breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused, repeats=repeat_info, cold=cold,
+                settle_steps=settle_steps)
+
+
+def cold_pair(args, torch, step, layers, weights, x0, ws, outs, flops, gemm_us_hot, i_dom):
+    """The same steps rotating over copies of every weight blob, input, workspace
+    and output, enough that the copies exceed the 256 MB last-level cache three
+    times over: a step's operands were last touched two or more steps earlier and
+    have been evicted by the others, so they come from HBM."""
+    per_set = sum(t.numel() * t.element_size() for t in list(weights) + [x0] + list(ws) + list(outs))
+    nsets = max(3, -(-(3 * (256 << 20)) // per_set))
+    sets = [(list(weights), x0, list(ws), list(outs))]
+    for _ in range(nsets - 1):
+        sets.append(([w.clone() for w in weights], x0.clone(), [torch.empty_like(t) for t in ws],
+                     [torch.empty_like(t) for t in outs]))
+    n = len(layers)
+    for k in range(nsets):
+        step(opset=sets[k])
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] for _ in range(args.steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(args.steps):
+        step(evs[k], opset=sets[k % nsets])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    g_us = [sum(evs[k][i][1].elapsed_time(evs[k][i][2]) for k in range(args.steps)) * 1e3 / args.steps
+            for i in range(n)]
+    q_us = [sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) * 1e3 / args.steps
+            for i in range(n)]
+    del sets
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
+            "operand_sets": nsets, "bytes_per_set": per_set, "gemm_us": [round(x, 2) for x in g_us],
+            "quantize_us": [round(x, 2) for x in q_us], "dominant_gemm_us": round(g_us[i_dom], 2),
+            "dominant_gemm_us_hot": round(gemm_us_hot[i_dom], 2)}
+
+
+def shader_clock():
+    """rocm-smi's current shader clock line(s), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l.lower()]
+        return lines[:2] or None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def w4a16_bytes(M, K, N):
@@ -225,6 +390,12 @@ def gpu_leg_w4a16(args):
         it[0] += 1
         sq.gemm_w4a16(layer, w, x, sq.EPI_BIAS, out=out)
 
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms and settle_steps < 20000:
+        step()
+        settle_steps += 1
+        if settle_steps % 64 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -259,7 +430,8 @@ def gpu_leg_w4a16(args):
     breakdown = {spec.name: {"gemm_us": round(launch_us, 2), "GBps": round(achieved, 1),
                              "gemm_TFLOPs": round(flops / (launch_us * 1e-6) / 1e12, 3)}}
     return dict(value=flops / (ms_per_step * 1e-3) / 1e12, ms_per_step=ms_per_step, gpu_ms_per_step=None,
-                roofline=roofline, breakdown=breakdown, specs=[spec], fmt="bf16", fused=None)
+                roofline=roofline, breakdown=breakdown, specs=[spec], fmt="bf16", fused=None,
+                settle_steps=settle_steps)
 
 
 def cpu_baseline_w4a16(spec):
@@ -274,7 +446,7 @@ def cpu_baseline_w4a16(spec):
     W.forward(d["X"], d["W"], d["b"])
     secs = time.perf_counter() - t0
     return {"value": round(2.0 * spec.M * spec.N * spec.K / secs / 1e12, 6), "unit": "TOPS", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
             "sample": f"{spec.name}: all {spec.M} tokens x {spec.N} outputs (K={spec.K}); {secs:.1f} s of oracle "
                       "time (INT4 weight quantization, fp64 product, bias); quantization is single-threaded "
                       f"numpy, the product uses {threads} BLAS threads"}
@@ -354,7 +526,7 @@ def fused_pair(args, sq, torch, layers, weights, x, ws, outs, epis, M, flops):
                         "down-projection sum); fc2 gemm"}
 
 
-def cpu_baseline(specs, budget_rows=2048):
+def cpu_baseline(specs, ops, budget_rows=2048):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     `budget_rows` tokens of each layer against 1/2 (K <= 4096) or 1/8 of the
     output columns (about 10 s of host time), scaled to effective TOPS of the
@@ -366,8 +538,7 @@ def cpu_baseline(specs, budget_rows=2048):
 
     threads = _blas_threads()
     work, secs, parts = 0.0, 0.0, []
-    for spec in specs:
-        L = synth.draw_layer(spec)
+    for spec, L in zip(specs, ops):
         r = spec.rank + spec.lora_rank
         rows = np.arange(min(budget_rows, spec.M))
         ncols = max(16, spec.N // (2 if spec.K <= 4096 else 8))
@@ -378,11 +549,11 @@ def cpu_baseline(specs, budget_rows=2048):
         secs += time.perf_counter() - t0
         work += 2.0 * rows.size * ncols * spec.K
         parts.append(f"{spec.name}: {rows.size} tokens x {ncols} outputs (K={spec.K}, r={r})")
-        del L
     return {"value": round(work / secs / 1e12, 6), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
             "sample": "; ".join(parts) + f"; {secs:.1f} s of oracle time (quantize both operands, fp64 product, "
                       "low-rank branch, bias, GELU); quantization is single-threaded numpy, the product uses "
-                      f"{threads} BLAS threads"}
+                      f"{threads} BLAS threads on a host with {len(os.sched_getaffinity(0))} CPUs"}
 
 
 def main():
@@ -393,12 +564,21 @@ def main():
               "this measurement).", file=sys.stderr)
         sys.exit(2)
     w4a16 = args.workload in W4A16
-    r = gpu_leg_w4a16(args) if w4a16 else gpu_leg(args)
+    clock_before = shader_clock()
+    if w4a16:
+        r = gpu_leg_w4a16(args)
+        ops = None
+    else:
+        ops = layer_operands(layers_of(args.workload), args.operands)
+        r = gpu_leg(args, ops)
+    clock_after = shader_clock()
     specs = r["specs"]
     cfg = {"workload": args.workload, "layers": [
         {"name": s.name, "M": s.M, "K": s.K, "N": s.N, "rank": s.rank + s.lora_rank, "fmt": s.fmt,
          "epilogue": "bias" if w4a16 else "lowrank+bias" + ("+gelu" if s.gelu else "")} for s in specs],
         "output": "bf16", "weights": "packed once before timing"}
+    if not w4a16:
+        cfg["operands"] = args.operands
     if w4a16:
         cfg["activations"] = "bf16 (W4A16)"
     line = {
@@ -411,8 +591,15 @@ def main():
         line["gpu_ms_per_step"] = round(r["gpu_ms_per_step"], 4)
     if r["fused"] is not None:
         line["fused_mlp" if args.workload == "mlp_mxfp4" else "fused_qkv"] = r["fused"]
+    if r.get("repeats") is not None:
+        line["repeats"] = r["repeats"]
+    if r.get("cold") is not None:
+        line["cold"] = r["cold"]
+    if r.get("settle_steps") is not None:
+        line["clock_settle"] = {"ms": args.settle_ms, "untimed_steps": r["settle_steps"]}
+    line["clock"] = {"before": clock_before, "after": clock_after}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_w4a16(specs[0]) if w4a16 else cpu_baseline(specs)
+        line["cpu_baseline"] = cpu_baseline_w4a16(specs[0]) if w4a16 else cpu_baseline(specs, ops)
     print(json.dumps(line), flush=True)
 
 
