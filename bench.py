@@ -344,14 +344,19 @@ def cold_pair(args, torch, step, layers, weights, x0, ws, outs, flops, gemm_us_h
 
 
 def shader_clock():
-    """rocm-smi's current shader clock line(s), or None."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
-        lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l.lower()]
-        return lines[:2] or None
-    except (OSError, subprocess.SubprocessError):
-        return None
+    """The GPU's current shader clock from the amdgpu driver's sysfs files
+    (the starred pp_dpm_sclk level), or None.  Read in-process: a child
+    program started after the GPU is initialised is not wanted here."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                cur = [l.strip() for l in f if l.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            return [f"{path.split('/')[4]}: {c}" for c in cur]
+    return None
 
 
 def w4a16_bytes(M, K, N):
