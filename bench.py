@@ -73,7 +73,157 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the timed region, copy MIB mebibytes device to device once (a plain copy of "
                         "known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="no benchmark: summarize rocprofv3 --pmc output directories of this script's runs "
+                        "(a markdown table per kernel role on stdout)")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="no benchmark: launch durations per kernel role from a rocprofv3 --kernel-trace output "
+                        "directory of this script's runs (markdown on stdout)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no benchmark: HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE run made with "
+                        "--copy-calibration; prints the table and rewrites profiles/traffic.json")
     return p.parse_args()
+
+
+# ---- rocprofv3 counter summaries (host only) ----
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "*counter_collection.csv"))):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    name = name.replace("void ", "").replace("svdq::", "")
+    return name[:name.index("(")] if "(" in name else name
+
+
+def _dispatch_roles(rows):
+    """{dispatch id: role}.  GEMM launches are named by their kernel; an
+    activation quantize or down-projection sum belongs to the next GEMM
+    launched after it (bench.py runs each layer's launches back to back),
+    except a sum launched right after a GEMM, which finishes that GEMM's
+    fused quantization of the next layer's input."""
+    order = {}
+    for r in rows:
+        order.setdefault(int(r["Dispatch_Id"]), _short(r["Kernel_Name"]))
+    roles, pending, prev = {}, [], ""
+    for did in sorted(order):
+        k = order[did]
+        if k.startswith("gemm_"):
+            roles[did] = k
+            for p, pk in pending:
+                roles[p] = f"{pk} -> {k}"
+            pending = []
+        elif k.startswith("reduce_down_kernel") and prev.startswith("gemm_"):
+            roles[did] = f"{k} <- {prev}"
+        elif k.startswith(("quantize_act_kernel", "reduce_down_kernel")):
+            pending.append((did, k))
+        prev = k
+    return roles
+
+
+def _per_role(rows, counters):
+    import collections
+    roles = _dispatch_roles(rows)
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    n = collections.defaultdict(set)
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        if did not in roles or r["Counter_Name"] not in counters:
+            continue
+        acc[roles[did]][r["Counter_Name"]] += float(r["Counter_Value"])
+        n[roles[did]].add(did)
+    return {k: {c: v / len(n[k]) for c, v in cs.items()} for k, cs in acc.items()}, {k: len(v) for k, v in n.items()}
+
+
+def summarize_counters(dirs):
+    """Mean per launch of every counter, and the derived figures: cycles =
+    GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / cycles; VALU issue = SQ_INSTS_VALU /
+    256 CUs / cycles (a CU issues at most one wave64 VALU instruction per
+    cycle); LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; waiting =
+    SQ_WAIT_ANY / SQ_WAVE_CYCLES."""
+    merged, counts = {}, {}
+    for d in dirs:
+        rows = _counter_rows(d)
+        names = {r["Counter_Name"] for r in rows}
+        per, cnt = _per_role(rows, names)
+        for k, cs in per.items():
+            merged.setdefault(k, {}).update(cs)
+            counts[k] = max(counts.get(k, 0), cnt[k])
+    print("| kernel (launches) | cycles | MFMA busy | VALU issue | VALU / MFMA instr | LDS conflict | waiting |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(merged):
+        c = merged[k]
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+        f = lambda v: "-" if v is None else f"{v:.1%}"
+        mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / cyc if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c else None
+        vi = c["SQ_INSTS_VALU"] / 256 / cyc if cyc and "SQ_INSTS_VALU" in c else None
+        vpm = (f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.1f}" if c.get("SQ_INSTS_MFMA") else "-")
+        lc = (c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"] if c.get("SQ_LDS_IDX_ACTIVE") else None)
+        wt = (c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else None)
+        print(f"| `{k}` ({counts[k]}) | {cyc:.0f} | {f(mb)} | {f(vi)} | {vpm} | {f(lc)} | {f(wt)} |")
+    print()
+    print("Raw means per launch:")
+    for k in sorted(merged):
+        print(f"- `{k}`: " + ", ".join(f"{c} {v:.0f}" for c, v in sorted(merged[k].items())))
+
+
+def summarize_trace(d):
+    """Mean, min and max duration per kernel role over every launch of a
+    kernel-trace run (settle, warmup, timed and breakdown passes alike)."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "*kernel_trace.csv"))):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    roles = _dispatch_roles(rows)
+    dur = {}
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        if did in roles:
+            dur.setdefault(roles[did], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel role | launches | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for k in sorted(dur):
+        v = dur[k]
+        print(f"| `{k}` | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | {min(v):.1f} | "
+              f"{max(v):.1f} |")
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Read and written HBM bytes per launch of the pair's kernels, scaled by
+    what the same counters read for the 256 MiB calibration copy (the largest
+    __amd_rocclr_copyBuffer launch)."""
+    res = {}
+    for which, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]
+                  and int(r["Grid_Size"]) == max(int(x["Grid_Size"]) for x in rows if "copyBuffer" in x["Kernel_Name"])]
+        scale = (256 * 1024) / copies[-1]
+        per, cnt = _per_role(rows, {"FETCH_SIZE", "WRITE_SIZE"})
+        for k, cs in per.items():
+            v = next(iter(cs.values()))
+            res.setdefault(k, {})[which] = (v, scale, cnt[k])
+    print("| kernel (launches) | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB | total MB |")
+    print("|---|---|---|---|---|---|")
+    out = {}
+    for k in sorted(res):
+        (fv, fs, n), (wv, ws, _) = res[k]["fetch"], res[k]["write"]
+        rb, wb = fv * fs * 1024, wv * ws * 1024
+        print(f"| `{k}` ({n}) | {fv:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
+        out[k] = {"fetch_kib_counter": round(fv, 1), "write_kib_counter": round(wv, 1), "fetch_scale": round(fs, 4),
+                  "write_scale": round(ws, 4), "read_bytes": int(rb), "write_bytes": int(wb),
+                  "bytes_per_launch": int(rb + wb), "launches": n}
+    print(f"\nscales: FETCH_SIZE x{res[next(iter(res))]['fetch'][1]:.4f}, WRITE_SIZE x{res[next(iter(res))]['write'][1]:.4f}")
+    return out
 
 
 def layers_of(workload):
@@ -563,6 +713,20 @@ def cpu_baseline(specs, ops, budget_rows=2048):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.traffic_from:
+        t = traffic_from(*args.traffic_from)
+        names = {"gemm_mxfp4_kernel<4, 4, false, true, -1, false, 4>": "mlp_mxfp4:gemm_mxfp4_fc1_mxfp4",
+                 "gemm_mxfp4_kernel<8, 8, false, false, -1, false, 7>": "mlp_mxfp4:gemm_mxfp4_fc2_mxfp4"}
+        d = {names[k]: dict(v, gemm_source_sha256_16=gemm_source_hash()) for k, v in t.items() if k in names}
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+            json.dump(d, f, indent=1)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the layer runs on "
               "a single GPU (token-parallel sharding needs no collective, so N GPUs are N copies of "
