@@ -167,7 +167,8 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
  *     (z[2p], z[2p+1]) -> (z[2p] c - z[2p+1] s, z[2p] s + z[2p+1] c),
  *     c = rope_cos[m][p], s = rope_sin[m][p];
  * V heads are y.  Y receives the bf16 (nearest even) result, M x N, row stride ldy.
- *   head_dim  must be 128; N a multiple of 384; MXFP4 only (else SVDQ_ERR_FORMAT)
+ *   head_dim  must be 128; N a multiple of 384; any of the three formats (the
+ *             Diffusers page names INT4 and NVFP4 kernels; the epilogue is the same)
  *   norm_q, norm_k  device, bf16 bits [128], 16-byte aligned
  *   eps       in [0, 1]
  *   rope_cos, rope_sin  device, float32, M x 64 row-major (angle of pair p of token m),

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 105
+    assert L.svdq_version() == 106
     for s in range(9):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -170,7 +170,9 @@ def test_gemm_qkv_validation(L, forced_device_error):
     assert f(ctypes.byref(D(K=1024, N=512)), P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P, 512, None) == 2
     assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(-1.0), P, P, P, 768, None) == 2       # eps
     assert f(d, P, P, 4, 7, 128, P, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 3       # GELU flag
-    assert f(ctypes.byref(D(fmt=2, K=1024, N=768)), *ok) == 3                                 # INT4
+    assert f(ctypes.byref(D(fmt=2, K=1024, N=768)), *ok) == 6                                 # INT4 served
+    assert f(ctypes.byref(D(fmt=3, K=1024, N=768)), *ok) == 6                                 # NVFP4 served
+    assert f(ctypes.byref(D(fmt=4, K=1024, N=768)), *ok) == 3                                 # no such format
     assert f(d, P, P, 4, 3, 128, P + 8, P, ctypes.c_float(1e-6), P, P, P, 768, None) == 4   # norm_q aligned
     assert f(d, P, P, 4, 3, 128, P, P, ctypes.c_float(1e-6), P, P, P + 8, 768, None) == 4   # Y aligned
 

@@ -2,7 +2,8 @@
 normalization and the rotary embedding in the GEMM epilogue, against the
 oracle's layer output passed through oracle/qkv.py (float64), element by
 element at a medium size and on sampled tokens (all of their heads) at the
-FLUX QKV size.  The V heads must equal svdq_gemm's bf16 output bit for bit."""
+FLUX QKV size, in every format.  The V heads must equal svdq_gemm's bf16
+output bit for bit."""
 import numpy as np
 import pytest
 
@@ -58,17 +59,23 @@ QKV_CASES = [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0,
              (2048, 512, 6144, 16, 4)] + _random_cases(4, 2028)
 
 
-@pytest.mark.parametrize("M,K,N,rank,seed", QKV_CASES)
-def test_qkv_elementwise(torch_dev, M, K, N, rank, seed):
+# every format: MXFP4 on all cases; INT4 and NVFP4 (their GEMMs take 128 x 128
+# tiles at every size) on the first three and two of the random shapes
+FMT_CASES = ([("mxfp4",) + c for c in QKV_CASES] +
+             [(f,) + c for f in ("int4", "nvfp4") for c in QKV_CASES[:3] + QKV_CASES[4:6]])
+
+
+@pytest.mark.parametrize("fmt,M,K,N,rank,seed", FMT_CASES)
+def test_qkv_elementwise(torch_dev, fmt, M, K, N, rank, seed):
     torch, dev = torch_dev
     spec = synth.layer_spec("qkv", M=M, K=K, N=N, rank=rank, x_outliers=max(1, K // 100),
                             w_outliers=max(1, K // 100), lora_rank=0)
     L = synth.draw_layer(spec, seed=seed)
     E = synth.draw_qkv_extras(M, seed=seed)
-    layer = sq.Layer("mxfp4", K, N, rank)
-    print(f"qkv M={M} K={K} N={N} r={rank}", flush=True)
+    layer = sq.Layer(fmt, K, N, rank)
+    print(f"qkv {fmt} M={M} K={K} N={N} r={rank}", flush=True)
     Yq, Yp = _run(torch, dev, L, E, layer, M)
-    Y_o = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")["Y"]
+    Y_o = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], fmt)["Y"]
     want = _oracle(Y_o, E)
     got = bf16_to_np(Yq)
     hd = N // 3
@@ -77,18 +84,19 @@ def test_qkv_elementwise(torch_dev, M, K, N, rank, seed):
     assert torch.equal(Yq[:, 2 * hd:].view(torch.int16), Yp[:, 2 * hd:].view(torch.int16)), "V differs from svdq_gemm"
 
 
-def test_qkv_full_size_sampled_tokens(torch_dev):
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+def test_qkv_full_size_sampled_tokens(torch_dev, fmt):
     """FLUX QKV: M=4608, K=3072 -> N=9216 (24 heads each of Q, K, V), rank 32."""
     torch, dev = torch_dev
     spec = synth.CONFIGS["qkv"]
     L = synth.draw_layer(spec)
     E = synth.draw_qkv_extras(spec.M, seed=7)
-    layer = sq.Layer("mxfp4", spec.K, spec.N, spec.rank)
-    print("qkv full size", flush=True)
+    layer = sq.Layer(fmt, spec.K, spec.N, spec.rank)
+    print(f"qkv full size {fmt}", flush=True)
     Yq, Yp = _run(torch, dev, L, E, layer, spec.M)
     rng = np.random.default_rng(99)
     rows = np.unique(np.concatenate([[0, spec.M - 1], rng.choice(spec.M, 30, replace=False)]))
-    Y_o = Ly.forward_rows(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4", rows)
+    Y_o = Ly.forward_rows(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], fmt, rows)
     Es = dict(E, cos=E["cos"][rows], sin=E["sin"][rows])
     want = _oracle(Y_o, Es)
     got = bf16_to_np(Yq)[rows]

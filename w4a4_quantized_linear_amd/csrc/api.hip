@@ -23,8 +23,9 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
 hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                              int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
                              uint8_t* nact, const ActLayout& nal, hipStream_t s);
-hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
-                           int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, const uint16_t* norm_q,
+hipError_t launch_gemm_qkv(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act,
+                           const ActLayout& al, int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi,
+                           const uint16_t* norm_q,
                            const uint16_t* norm_k, float eps, const float* rope_cos, const float* rope_sin,
                            hipStream_t s);
 hipError_t launch_gemm_w4a16(const uint8_t* wblob, const WeightLayout& wl, int K, int N, const uint16_t* X,
@@ -137,7 +138,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 105; }
+int svdq_version(void) { return 106; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -255,7 +256,7 @@ svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const 
       !(eps >= 0.0f && eps <= 1.0f))
     return SVDQ_ERR_SHAPE;
   if ((s = check_fmt(d)) != SVDQ_OK) return s;
-  if (d->fmt != SVDQ_MXFP4 || (epi & ~(SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS)) != 0) return SVDQ_ERR_FORMAT;
+  if ((epi & ~(SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS)) != 0) return SVDQ_ERR_FORMAT;
   if (!aligned(w_packed, 256) || !aligned(a_packed, 256) || !aligned(norm_q, 16) || !aligned(norm_k, 16) ||
       (M > 0 && (!aligned(Y, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))) || ldy % 8 != 0)
     return SVDQ_ERR_ALIGN;
@@ -263,7 +264,7 @@ svdq_status svdq_gemm_qkv(const svdq_layer_desc* d, const void* w_packed, const 
   if (M == 0) return SVDQ_OK;
   const WeightLayout wl = weight_layout(d->fmt, d->K, d->N, d->rank);
   const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
-  return launched(launch_gemm_qkv(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
+  return launched(launch_gemm_qkv(d->fmt, static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                   al, d->K, d->N, M, Y, ldy, epi, norm_q, norm_k, eps, rope_cos, rope_sin,
                                   static_cast<hipStream_t>(stream)));
 }

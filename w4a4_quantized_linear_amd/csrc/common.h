@@ -56,18 +56,24 @@ __device__ __forceinline__ uint32_t e8m0_of_amax(float amax) {
   const int be = int((__float_as_uint(amax) >> 23) & 0xFFu);
   return uint32_t(be > 2 ? be - 2 : 0);
 }
-// 2^-e as fp32 for a scale byte b (e = b - 127); exact for every b in [0, 254].
-__device__ __forceinline__ float inv_scale_of_e8m0(uint32_t b) {
-  // 2^(127 - b) has biased exponent 254 - b; scale bytes from e8m0_of_amax are at
-  // most 252, so the result is a normal power of two in [2^-125, 2^127].
-  return __uint_as_float((254u - b) << 23);
-}
+
+// The scale byte b as the gfx950 convert's scale operand: the convert divides by
+// 2^(E - 127), E the operand's fp32 exponent field, before rounding, so the byte
+// goes into that field (b = 0 gives +0.0, i.e. 2^-127).  The division by a power
+// of two is exact, so cvt_fp4x2_div(.., x, y, scale_operand(b)) encodes exactly
+// x * 2^(127 - b), with no multiply (and no underflow of that product) in fp32.
+__device__ __forceinline__ float scale_operand(uint32_t b) { return __uint_as_float(b << 23); }
 
 // Two fp32 -> packed E2M1 pair in byte `sel` of `old` (nearest, ties to even,
 // saturating at 6, sign copied): the gfx950 convert with unit scale.
 template <int SEL>
 __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+// The same of a / 2^(E - 127) and b / 2^(E - 127), E the exponent field of s.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2_div(uint32_t old, float a, float b, float s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, s, SEL);
 }
 
 template <int SEL>

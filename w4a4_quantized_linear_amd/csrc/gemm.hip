@@ -267,12 +267,12 @@ __device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slo
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
         amax = rowgroup_max(amax);
         const uint32_t sb = e8m0_of_amax(amax);
-        const float inv = inv_scale_of_e8m0(sb);
+        const float so = scale_operand(sb);
         uint32_t cw = 0;
-        cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
-        cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
-        cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
-        cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+        cw = cvt_fp4x2_div<0>(cw, x[8 * h + 0], x[8 * h + 1], so);
+        cw = cvt_fp4x2_div<1>(cw, x[8 * h + 2], x[8 * h + 3], so);
+        cw = cvt_fp4x2_div<2>(cw, x[8 * h + 4], x[8 * h + 5], so);
+        cw = cvt_fp4x2_div<3>(cw, x[8 * h + 6], x[8 * h + 7], so);
         // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
         *reinterpret_cast<uint32_t*>(codes + code_chunk(m / 16, kb / 4, K2, (kb & 3) * 16 + r) + c * 4) = cw;
         if (c == (kb & 3)) scales[mx_scale_byte(m, kb, K2)] = uint8_t(sb);
@@ -744,7 +744,7 @@ struct Int4Stage {
   uint32_t sx[WM];        // activation scales: the lane's row x 2 groups (fp16)
 };
 
-template <int WN, int WM, bool OUT_F32, bool GELU>
+template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false>
 __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
@@ -827,7 +827,15 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
     compute(s1);
   }
   __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
-  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+  if constexpr (QKV) {
+    static_assert(!OUT_F32 && !GELU, "the QKV epilogue stores bf16 with no activation");
+    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    float bv[WN][4];
+    load_bias<WN>(g, n0, lane, bv);
+    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, stage + w * 32 * stage_row_bytes<WN>());
+  } else {
+    epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+  }
 }
 
 // ------------------------------------------------------------------ NVFP4
@@ -873,7 +881,7 @@ struct Nv4Stage {
   uint32_t sw[WN], sx[WM];    // the lane's two E4M3 group scales per fragment
 };
 
-template <int WN, int WM, bool OUT_F32, bool GELU>
+template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false>
 __global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
@@ -958,7 +966,15 @@ __global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = acc[i][j] * gs;
   __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
-  epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+  if constexpr (QKV) {
+    static_assert(!OUT_F32 && !GELU, "the QKV epilogue stores bf16 with no activation");
+    add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+    float bv[WN][4];
+    load_bias<WN>(g, n0, lane, bv);
+    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, stage + w * 32 * stage_row_bytes<WN>());
+  } else {
+    epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+  }
 }
 
 // ------------------------------------------------------------------ W4A16
@@ -1308,10 +1324,13 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
 
 hipError_t launch_reduce_down(const float* part, int splits, int64_t rows_pad, int r_pad, uint16_t* Dout, hipStream_t s);
 
-// The GEMM of a fused QKV layer (MXFP4, head dim 128) with the Q/K
-// normalization and rotary embedding in its epilogue; bf16 output.
-hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
-                           int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, const uint16_t* norm_q,
+// The GEMM of a fused QKV layer (head dim 128) with the Q/K normalization and
+// rotary embedding in its epilogue; bf16 output.  Every format: the INT4 and
+// NVFP4 kernels (128 x 128 tiles, a head split between two waves) take the same
+// epilogue as the MXFP4 kernel's 128 x 128 tiles.
+hipError_t launch_gemm_qkv(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act,
+                           const ActLayout& al, int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi,
+                           const uint16_t* norm_q,
                            const uint16_t* norm_k, float eps, const float* rope_cos, const float* rope_sin,
                            hipStream_t s) {
   GemmArgs g{};
@@ -1324,8 +1343,13 @@ hipError_t launch_gemm_qkv(const uint8_t* wblob, const WeightLayout& wl, const u
   g.epi = epi;
   g.Y = Y;
   g.norm_q = norm_q; g.norm_k = norm_k; g.rope_cos = rope_cos; g.rope_sin = rope_sin; g.eps = eps;
+  g.w_amax = wl.amax;
   const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-  if (use_big_tiles(big))
+  if (fmt == kFmtINT4)
+    hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, false, true>), dim3(big * 4), dim3(256), 0, s, g);
+  else if (fmt == kFmtNVFP4)
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<4, 4, false, false, true>), dim3(big * 4), dim3(256), 0, s, g);
+  else if (use_big_tiles(big))
     hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(big), dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, -1, true>), dim3(big * 4), dim3(256), 0, s, g);

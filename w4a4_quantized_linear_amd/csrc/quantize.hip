@@ -61,12 +61,12 @@ __global__ void __launch_bounds__(512) quantize_weight_kernel(const float* __res
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           amax = fmaxf(amax, __shfl_xor(amax, 32));
           const uint32_t sb = e8m0_of_amax(amax);
-          const float inv = inv_scale_of_e8m0(sb);
+          const float so = scale_operand(sb);
           uint32_t cw = 0;
-          cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
-          cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
-          cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
-          cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+          cw = cvt_fp4x2_div<0>(cw, x[8 * h + 0], x[8 * h + 1], so);
+          cw = cvt_fp4x2_div<1>(cw, x[8 * h + 2], x[8 * h + 3], so);
+          cw = cvt_fp4x2_div<2>(cw, x[8 * h + 4], x[8 * h + 5], so);
+          cw = cvt_fp4x2_div<3>(cw, x[8 * h + 6], x[8 * h + 7], so);
           const int ks = kc * 4 + jb / 4;
           *reinterpret_cast<uint32_t*>(codes + code_chunk(rt, ks, K, (jb & 3) * 16 + row) + c * 4) = cw;
           if ((jb & 3) == c) sdw |= sb << (8 * (jb >> 2));
@@ -276,12 +276,12 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
         amax = rowgroup_max(amax);
         const uint32_t sb = e8m0_of_amax(amax);
-        const float inv = inv_scale_of_e8m0(sb);
+        const float so = scale_operand(sb);
         uint32_t cw = 0;
-        cw = cvt_fp4x2<0>(cw, x[8 * h + 0] * inv, x[8 * h + 1] * inv);
-        cw = cvt_fp4x2<1>(cw, x[8 * h + 2] * inv, x[8 * h + 3] * inv);
-        cw = cvt_fp4x2<2>(cw, x[8 * h + 4] * inv, x[8 * h + 5] * inv);
-        cw = cvt_fp4x2<3>(cw, x[8 * h + 6] * inv, x[8 * h + 7] * inv);
+        cw = cvt_fp4x2_div<0>(cw, x[8 * h + 0], x[8 * h + 1], so);
+        cw = cvt_fp4x2_div<1>(cw, x[8 * h + 2], x[8 * h + 3], so);
+        cw = cvt_fp4x2_div<2>(cw, x[8 * h + 4], x[8 * h + 5], so);
+        cw = cvt_fp4x2_div<3>(cw, x[8 * h + 6], x[8 * h + 7], so);
         // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
         __builtin_amdgcn_raw_buffer_store_b32(cw, rC, uint32_t(row * 16 + c * 4),
                                               uint32_t(ks * 1024 + (kb & 3) * 256), 0);
