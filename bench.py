@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="mlp_mxfp4", choices=list(PAIRS) + list(SINGLE) + list(W4A16))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fmt", choices=["mxfp4", "int4", "nvfp4"], default=None,
+                   help="4-bit format of every layer of the workload (default: the workload's own)")
     p.add_argument("--operands", default="calibrated", choices=["calibrated", "drawn"],
                    help="layer operands: converted from the dense draw (default) or drawn look-alikes")
     p.add_argument("--no-cold", action="store_true", help="skip the cold (operand-rotating) timing")
@@ -226,10 +228,12 @@ def traffic_from(fetch_dir, write_dir):
     return out
 
 
-def layers_of(workload):
+def layers_of(workload, fmt=None):
+    import dataclasses
     import synth
     names = PAIRS.get(workload, (workload,))
-    return [synth.CONFIGS[n] for n in names]
+    specs = [synth.CONFIGS[n] for n in names]
+    return [dataclasses.replace(s, fmt=fmt) for s in specs] if fmt else specs
 
 
 def gemm_source_hash() -> str:
@@ -328,7 +332,7 @@ def gpu_leg(args, ops):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    specs = layers_of(args.workload)
+    specs = layers_of(args.workload, args.fmt)
     layers, weights, inputs = [], [], []
     for i, spec in enumerate(specs):
         L = ops[i]
@@ -738,7 +742,7 @@ def main():
         r = gpu_leg_w4a16(args)
         ops = None
     else:
-        ops = layer_operands(layers_of(args.workload), args.operands)
+        ops = layer_operands(layers_of(args.workload, args.fmt), args.operands)
         r = gpu_leg(args, ops)
     clock_after = shader_clock()
     specs = r["specs"]
