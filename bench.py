@@ -16,7 +16,7 @@ With --workload mod_w4a16 the step is one W4A16 launch (svdq_gemm_w4a16: bf16
 activations times INT4 weights, the memory-bound modulation projection) and
 `roofline` is HBM-bound: algorithmic bytes (codes, scales, X, Y, bias) per
 launch over its event-timed duration.
-For the MXFP4 pair, `fused_mlp` times the same pair with fc1's GEMM quantizing
+For the MXFP4 and INT4 pairs, `fused_mlp` times the same pair with fc1's GEMM quantizing
 its output for fc2 in its epilogue (svdq_gemm_quant: three launches plus the
 down-projection sum instead of four), same inputs, same step count.
 
@@ -453,7 +453,7 @@ def gpu_leg(args, ops):
     cold = None if args.no_cold else cold_pair(args, torch, step, layers, weights, inputs[0], ws, outs,
                                                 sum(flops), gemm_us, i_dom)
     fused = None
-    if args.workload == "mlp_mxfp4":
+    if len(layers) == 2 and layers[0].fmt == layers[1].fmt and layers[0].fmt in ("mxfp4", "int4"):
         fused = fused_pair(args, sq, torch, layers, weights, inputs[0], ws, outs, epis, M, sum(flops))
     elif args.workload == "qkv":
         fused = fused_qkv(args, sq, synth, torch, np, layers[0], weights[0], inputs[0], ws[0], outs[0], epis[0], M,
@@ -763,7 +763,7 @@ def main():
     if r["gpu_ms_per_step"] is not None:
         line["gpu_ms_per_step"] = round(r["gpu_ms_per_step"], 4)
     if r["fused"] is not None:
-        line["fused_mlp" if args.workload == "mlp_mxfp4" else "fused_qkv"] = r["fused"]
+        line["fused_mlp" if len(specs) == 2 else "fused_qkv"] = r["fused"]
     if r.get("repeats") is not None:
         line["repeats"] = r["repeats"]
     if r.get("cold") is not None:

@@ -146,12 +146,13 @@ svdq_status svdq_gemm(const svdq_layer_desc* d, const void* w_packed, const void
  * and scales bit for bit, and D' = H_hat L1' summed in a different (fixed) order
  * (one fp32 partial per output tile column of H, 128 or 256 columns, added in
  * column order by a second launch).  svdq_gemm(dn, wn_packed, an_packed, ...) then completes dn.  H itself
- * is never written.
+ * is never written.  The Diffusers page's kernels are INT4 (and NVFP4 on Blackwell):
+ * INT4 pairs are served as well as MXFP4 ones.
  *   d, w_packed, a_packed  layer d as for svdq_gemm (a_packed from svdq_quantize_act)
  *   epi       SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU (no SVDQ_EPI_OUT_F32)
  *   dn, wn_packed  the next layer and its packed weights
  *   an_packed device, svdq_act_bytes(dn, M) bytes, 256-byte aligned
- * Both layers MXFP4 (else SVDQ_ERR_FORMAT); dn->K != d->N or dn->rank > 64 give
+ * Both layers MXFP4 or both INT4 (else SVDQ_ERR_FORMAT); dn->K != d->N or dn->rank > 64 give
  * SVDQ_ERR_SHAPE; other checks and errors as svdq_gemm. */
 svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, const void* a_packed, int64_t M,
                             uint32_t epi, const svdq_layer_desc* dn, const void* wn_packed, void* an_packed,

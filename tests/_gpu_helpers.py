@@ -75,19 +75,23 @@ def check_bf16_output(Yb, Y_o, what):
     return mean_rel
 
 
-def check_chain_output(Y, Y_o, what):
+def check_chain_output(Y, Y_o, what, fmt="mxfp4"):
     """Output of a chain of layers where each side feeds its own intermediate
     (GPU H vs oracle H) to the next 4-bit quantizer.  Intermediates that differ
     by rounding flip a few 4-bit codes, and one flip moves a product term by a
     whole quantization step, so the per-element max bound does not carry over;
     the mean relative error bound does.  Checked: mean relative error <= 5e-3,
-    at most 0.1% of elements beyond 2e-2 rms, none beyond 0.25 rms."""
+    at most 0.1% of elements beyond 2e-2 rms (0.2% for INT4, whose uniform grid
+    of 15 steps per group puts more decision boundaries in the bulk of the
+    values than E2M1's, so the same differences in H flip more codes), none
+    beyond 0.25 rms."""
     Y = np.asarray(Y, dtype=np.float64)
     err = np.abs(Y - Y_o)
     rms = float(np.sqrt(np.mean(Y_o ** 2)))
     mean_rel = float(err.sum() / np.abs(Y_o).sum())
     frac = float(np.mean(err > Ly.MAX_OVER_RMS * rms))
-    assert mean_rel <= Ly.MEAN_REL and frac <= 1e-3 and err.max() <= 0.25 * rms, \
+    frac_max = 2e-3 if fmt == "int4" else 1e-3
+    assert mean_rel <= Ly.MEAN_REL and frac <= frac_max and err.max() <= 0.25 * rms, \
         f"{what}: mean rel {mean_rel:.2e}, fraction over 2e-2 rms {frac:.2e}, max/rms {err.max() / rms:.3f}"
     return mean_rel, frac
 

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.svdq_version() == 106
+    assert L.svdq_version() == 107
     for s in range(9):
         assert L.svdq_status_str(s)
     assert L.svdq_status_str(99) == b"unknown status"
@@ -150,8 +150,12 @@ def test_gemm_quant_validation(L, forced_device_error):
     assert q(d, P, P, 4, 7, ctypes.byref(D(K=1024, N=256)), P, P, None) == 2      # next K != N
     assert q(d, P, P, 4, 7, ctypes.byref(D(K=512, N=256, rank=80)), P, P, None) == 2  # next rank > 64
     assert q(d, P, P, -1, 7, dn, P, P, None) == 2
-    assert q(ctypes.byref(D(fmt=2, K=1024, N=512)), P, P, 4, 7, dn, P, P, None) == 3   # INT4 not fused
-    assert q(d, P, P, 4, 7, ctypes.byref(D(fmt=2, K=512, N=256)), P, P, None) == 3
+    assert q(ctypes.byref(D(fmt=2, K=1024, N=512)), P, P, 4, 7, dn, P, P, None) == 3   # INT4 into MXFP4
+    assert q(d, P, P, 4, 7, ctypes.byref(D(fmt=2, K=512, N=256)), P, P, None) == 3      # MXFP4 into INT4
+    assert q(ctypes.byref(D(fmt=3, K=1024, N=512)), P, P, 4, 7, ctypes.byref(D(fmt=3, K=512, N=256)), P, P,
+             None) == 3                                                                 # NVFP4 pairs
+    assert q(ctypes.byref(D(fmt=2, K=1024, N=512)), P, P, 4, 7, ctypes.byref(D(fmt=2, K=512, N=256, rank=32)),
+             P, P, None) == 6                                                           # INT4 pair served
     assert q(d, P, P, 4, 15, dn, P, P, None) == 3        # fp32 output flag
     assert q(d, P, P, 4, 7, dn, P, P + 16, None) == 4    # workspace not 256-aligned
     assert q(d, P, P, 4, 7, dn, P, P, None) == 6         # valid -> device check

@@ -112,7 +112,7 @@ def test_mlp_pair_chain(torch_dev, fmt):
     check_next_layer_on_gpu_h(torch, sq.unpack_act(l2, a2, 384), L2, H, Y2, fmt, np.arange(384),
                               "fc2 on the GPU's H")
     Y2_o = Ly.forward(F.bf16_bits(Y1_o), L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], fmt)["Y"]
-    check_chain_output(Y2.cpu().numpy(), Y2_o, "MLP pair output, each side on its own H")
+    check_chain_output(Y2.cpu().numpy(), Y2_o, "MLP pair output, each side on its own H", fmt)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4", "nvfp4"])

@@ -74,11 +74,11 @@ def _pair(M, K1, N1, r1, N2, r2, seed):
     return synth.draw_layer(s1, seed=seed), synth.draw_layer(s2, seed=seed + 100)
 
 
-def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, epi1=EPI1):
-    l1, l2 = sq.Layer("mxfp4", K1, N1, r1), sq.Layer("mxfp4", N1, N2, r2)
+def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, epi1=EPI1, fmt="mxfp4"):
+    l1, l2 = sq.Layer(fmt, K1, N1, r1), sq.Layer(fmt, N1, N2, r2)
     w1, w2 = pack(l1, L1, torch, dev), pack(l2, L2, torch, dev)
     a1 = sq.quantize_act(l1, w1, dev_tensor(L1["X"], torch, dev))
-    print(f"fused pair M={M} {K1}->{N1}->{N2} ranks {r1}/{r2} epi {epi1}", flush=True)
+    print(f"fused pair {fmt} M={M} {K1}->{N1}->{N2} ranks {r1}/{r2} epi {epi1}", flush=True)
     H = sq.gemm(l1, w1, a1, M, epi1)
     a2u = sq.quantize_act(l2, w2, H.view(torch.int16))
     a2f = sq.gemm_quant(l1, w1, a1, M, epi1, l2, w2)
@@ -86,7 +86,7 @@ def _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, epi1=EPI1):
     Y2u = sq.gemm(l2, w2, a2u, M, EPI2)
     Y2f = sq.gemm(l2, w2, a2f, M, EPI2)
     torch.cuda.synchronize()
-    return dict(H=H, uu=uu, uf=uf, Y2u=Y2u, Y2f=Y2f)
+    return dict(H=H, uu=uu, uf=uf, Y2u=Y2u, Y2f=Y2f, fmt=fmt)
 
 
 def _check_against_oracle(torch, r, L1, L2, M, what, rows=None, epi1=EPI1):
@@ -95,11 +95,12 @@ def _check_against_oracle(torch, r, L1, L2, M, what, rows=None, epi1=EPI1):
     judged on the input it actually received."""
     rows = np.arange(M) if rows is None else rows
     gelu = (epi1 & sq.EPI_GELU) != 0
+    fmt = r["fmt"]
     Y1_o = Ly.forward_rows(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"] if epi1 & sq.EPI_BIAS else None,
-                           "mxfp4", rows, gelu_act=gelu)
+                           fmt, rows, gelu_act=gelu)
     check_bf16_output(bf16_to_np(r["H"])[rows], Y1_o, f"{what}: first layer's H")
-    ref = check_next_layer_on_gpu_h(torch, r["uf"], L2, r["H"], r["Y2f"], "mxfp4", rows, f"{what}: fused")
-    check_next_layer_on_gpu_h(torch, r["uu"], L2, r["H"], r["Y2u"], "mxfp4", rows, f"{what}: unfused")
+    ref = check_next_layer_on_gpu_h(torch, r["uf"], L2, r["H"], r["Y2f"], fmt, rows, f"{what}: fused")
+    check_next_layer_on_gpu_h(torch, r["uu"], L2, r["H"], r["Y2u"], fmt, rows, f"{what}: unfused")
     return ref
 
 
@@ -121,18 +122,24 @@ def _check_against_unfused(torch, r, L2, r2, what):
     assert np.abs(yf - yu).max() <= 1e-4 * rms, f"{what}: next layer's output moved by {np.abs(yf - yu).max():.3e}"
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"M{c[0]}-{c[1]}-{c[2]}-{c[4]}-r{c[3]}-{c[5]}" for c in CASES])
-def test_fused_equals_unfused_and_oracle_chain(torch_dev, case):
+# MXFP4 on every case; INT4 (128 x 128 tiles at every size) on the fixed cases
+# and two of the random ones
+FMT_CASES = [("mxfp4", c) for c in CASES] + [("int4", c) for c in CASES[:5] + CASES[5:7]]
+
+
+@pytest.mark.parametrize("fmt,case", FMT_CASES,
+                         ids=[f"{f}-M{c[0]}-{c[1]}-{c[2]}-{c[4]}-r{c[3]}-{c[5]}" for f, c in FMT_CASES])
+def test_fused_equals_unfused_and_oracle_chain(torch_dev, fmt, case):
     torch, dev = torch_dev
     M, K1, N1, r1, N2, r2, seed = case
     L1, L2 = _pair(*case)
-    r = _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2)
+    r = _run(torch, dev, L1, L2, M, K1, N1, r1, N2, r2, fmt=fmt)
     _check_against_oracle(torch, r, L1, L2, M, f"case {case}")
     _check_against_unfused(torch, r, L2, r2, f"case {case}")
     # the chain through the oracle, which forms and quantizes its own H
-    Y1_o = Ly.forward(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"], "mxfp4", gelu_act=True)["Y"]
-    Y2_o = Ly.forward(F.bf16_bits(Y1_o), L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], "mxfp4")["Y"]
-    check_chain_output(r["Y2f"].cpu().numpy(), Y2_o, "fused MLP output")
+    Y1_o = Ly.forward(L1["X"], L1["lam"], L1["L1"], L1["L2"], L1["R"], L1["b"], fmt, gelu_act=True)["Y"]
+    Y2_o = Ly.forward(F.bf16_bits(Y1_o), L2["lam"], L2["L1"], L2["L2"], L2["R"], L2["b"], fmt)["Y"]
+    check_chain_output(r["Y2f"].cpu().numpy(), Y2_o, "fused MLP output", fmt)
 
 
 @pytest.mark.parametrize("case", [(300, 1024, 1024, 16, 512, 32, 11), (2048, 512, 4608, 32, 256, 16, 12)],
@@ -148,7 +155,8 @@ def test_fused_without_gelu(torch_dev, case):
     _check_against_unfused(torch, r, L2, case[5], f"no GELU, case {case}")
 
 
-def test_fused_ieee_division_path(torch_dev):
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4"])
+def test_fused_ieee_division_path(torch_dev, fmt):
     """A next-layer lambda outside [2^-32, 2^32] sends the whole layer to IEEE
     division; the fused codes still equal quantize_act's."""
     torch, dev = torch_dev
@@ -158,13 +166,13 @@ def test_fused_ieee_division_path(torch_dev):
     lam[3] = np.float32(2.0 ** 40)
     lam[700] = np.float32(2.0 ** -35)
     L2["lam"] = lam
-    r = _run(torch, dev, L1, L2, *case[:6])
+    r = _run(torch, dev, L1, L2, *case[:6], fmt=fmt)
     _check_against_oracle(torch, r, L1, L2, case[0], "lambda outside the fast range")
     _check_against_unfused(torch, r, L2, case[5], "lambda outside the fast range")
 
 
-@pytest.mark.parametrize("kind", ["calibrated", "drawn"])
-def test_fused_full_size_flux_mlp(torch_dev, kind):
+@pytest.mark.parametrize("fmt,kind", [("mxfp4", "calibrated"), ("mxfp4", "drawn"), ("int4", "calibrated")])
+def test_fused_full_size_flux_mlp(torch_dev, fmt, kind):
     """The FLUX MLP pair at its real size (fc1 4608 x 3072 -> 12288, GELU; fc2
     12288 -> 3072; rank 32), as the benchmark's fused step runs it, on the
     calibrated operands and on drawn ones: on sampled rows, H against the
@@ -172,13 +180,13 @@ def test_fused_full_size_flux_mlp(torch_dev, kind):
     fc2 on the GPU's H; on every row, codes and scales equal quantize_act's and
     D and fc2's output lie within bounds of the unfused path."""
     torch, dev = torch_dev
-    s1, s2 = synth.CONFIGS["fc1_mxfp4"], synth.CONFIGS["fc2_mxfp4"]
-    print(f"fused FLUX MLP pair, {kind} operands", flush=True)
+    s1, s2 = synth.CONFIGS[f"fc1_{fmt}"], synth.CONFIGS[f"fc2_{fmt}"]
+    print(f"fused FLUX MLP pair, {fmt}, {kind} operands", flush=True)
     if kind == "calibrated":
         L1, L2 = _calib.calibrated_layer(s1), _calib.calibrated_layer(s2)
     else:
         L1, L2 = synth.draw_layer(s1), synth.draw_layer(s2)
-    r = _run(torch, dev, L1, L2, s1.M, s1.K, s1.N, s1.rank, s2.N, s2.rank)
+    r = _run(torch, dev, L1, L2, s1.M, s1.K, s1.N, s1.rank, s2.N, s2.rank, fmt=fmt)
     rng = np.random.default_rng(78)
     rows = np.unique(np.concatenate([[0, s1.M - 1], rng.choice(s1.M, 30, replace=False)]))
     _check_against_oracle(torch, r, L1, L2, s1.M, f"FLUX MLP pair ({kind})", rows=rows)

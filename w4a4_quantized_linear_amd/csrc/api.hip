@@ -20,9 +20,9 @@ hipError_t launch_pack_aux(const uint16_t* L1, const uint16_t* L2, const float* 
                            int N, int rank, const WeightLayout& wl, uint8_t* blob, hipStream_t s);
 hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
                        int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi, hipStream_t s);
-hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
-                             int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
-                             uint8_t* nact, const ActLayout& nal, hipStream_t s);
+hipError_t launch_gemm_quant(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act,
+                             const ActLayout& al, int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob,
+                             const WeightLayout& nwl, uint8_t* nact, const ActLayout& nal, hipStream_t s);
 hipError_t launch_gemm_qkv(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act,
                            const ActLayout& al, int K, int N, int64_t M, void* Y, int64_t ldy, uint32_t epi,
                            const uint16_t* norm_q,
@@ -138,7 +138,7 @@ svdq_status check_gemm_args(const svdq_layer_desc* d, const void* w_packed, cons
 
 extern "C" {
 
-int svdq_version(void) { return 106; }
+int svdq_version(void) { return 107; }
 
 const char* svdq_status_str(svdq_status s) {
   switch (s) {
@@ -230,7 +230,7 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
   if (s != SVDQ_OK || (s = check_shape(dn)) != SVDQ_OK) return s;
   if (M < 0 || M > kMaxRows || dn->K != d->N || dn->rank > kGemmQuantMaxRank) return SVDQ_ERR_SHAPE;
   if ((s = check_fmt(d)) != SVDQ_OK || (s = check_fmt(dn)) != SVDQ_OK) return s;
-  if (d->fmt != SVDQ_MXFP4 || dn->fmt != SVDQ_MXFP4) return SVDQ_ERR_FORMAT;
+  if (d->fmt != dn->fmt || (d->fmt != SVDQ_MXFP4 && d->fmt != SVDQ_INT4_G64)) return SVDQ_ERR_FORMAT;
   if ((epi & ~(SVDQ_EPI_LOWRANK | SVDQ_EPI_BIAS | SVDQ_EPI_GELU)) != 0) return SVDQ_ERR_FORMAT;
   if (!aligned(w_packed, 256) || !aligned(a_packed, 256) || !aligned(wn_packed, 256) || !aligned(an_packed, 256))
     return SVDQ_ERR_ALIGN;
@@ -240,7 +240,7 @@ svdq_status svdq_gemm_quant(const svdq_layer_desc* d, const void* w_packed, cons
   const ActLayout al = act_layout(d->fmt, d->K, d->rank, M);
   const WeightLayout nwl = weight_layout(dn->fmt, dn->K, dn->N, dn->rank);
   const ActLayout nal = act_layout(dn->fmt, dn->K, dn->rank, M);
-  return launched(launch_gemm_quant(static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
+  return launched(launch_gemm_quant(d->fmt, static_cast<const uint8_t*>(w_packed), wl, static_cast<const uint8_t*>(a_packed),
                                     al, d->K, d->N, M, epi, static_cast<const uint8_t*>(wn_packed), nwl,
                                     static_cast<uint8_t*>(an_packed), nal, static_cast<hipStream_t>(stream)));
 }

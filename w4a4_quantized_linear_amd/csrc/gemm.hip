@@ -226,7 +226,7 @@ __device__ __forceinline__ void load_l1_next(const GemmArgs& g, int k0, int lane
 // every quotient by the two-operation form fma(x, r, x rl); otherwise by IEEE
 // division.  Both give the correctly rounded quotient wherever FAST is chosen
 // (see quant_h).
-template <int WN, int R16, bool FAST>
+template <int WN, int R16, bool FAST, int NFMT>
 __device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slot, int rbase, const float* lamv,
                                            int lane, int64_t mrow0, int k0, int tn,
                                            const uint4 (&l1r)[WN][R16 > 0 ? R16 : 1]) {
@@ -259,25 +259,58 @@ __device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slo
         const float a = ah[e >> 3][e & 7];
         x[e] = FAST ? fmaf(a, srl[kl], a * srlo[kl]) : a / slam[kl];
       }
+      if constexpr (NFMT == kFmtMXFP4) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kb = (k0 + s * 64 + h * 32) / 32;  // block index in the next layer's K
+        for (int h = 0; h < 2; ++h) {
+          const int kb = (k0 + s * 64 + h * 32) / 32;  // block index in the next layer's K
+          float amax = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+          amax = rowgroup_max(amax);
+          const uint32_t sb = e8m0_of_amax(amax);
+          const float so = scale_operand(sb);
+          uint32_t cw = 0;
+          cw = cvt_fp4x2_div<0>(cw, x[8 * h + 0], x[8 * h + 1], so);
+          cw = cvt_fp4x2_div<1>(cw, x[8 * h + 2], x[8 * h + 3], so);
+          cw = cvt_fp4x2_div<2>(cw, x[8 * h + 4], x[8 * h + 5], so);
+          cw = cvt_fp4x2_div<3>(cw, x[8 * h + 6], x[8 * h + 7], so);
+          // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
+          *reinterpret_cast<uint32_t*>(codes + code_chunk(m / 16, kb / 4, K2, (kb & 3) * 16 + r) + c * 4) = cw;
+          if (c == (kb & 3)) scales[mx_scale_byte(m, kb, K2)] = uint8_t(sb);
+        }
+      } else {
+        // INT4: the step is one 64-group, the activation kernel's rule: fp16
+        // scale amax / 7, codes rint(x / s) clamped to [-8, 7] (0 when s is 0)
+        const int kg = (k0 + s * 64) / 64;             // group index in the next layer's K
         float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[8 * h + e]));
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
         amax = rowgroup_max(amax);
-        const uint32_t sb = e8m0_of_amax(amax);
-        const float so = scale_operand(sb);
-        uint32_t cw = 0;
-        cw = cvt_fp4x2_div<0>(cw, x[8 * h + 0], x[8 * h + 1], so);
-        cw = cvt_fp4x2_div<1>(cw, x[8 * h + 2], x[8 * h + 3], so);
-        cw = cvt_fp4x2_div<2>(cw, x[8 * h + 4], x[8 * h + 5], so);
-        cw = cvt_fp4x2_div<3>(cw, x[8 * h + 6], x[8 * h + 7], so);
-        // lane chunk (kb & 3) * 16 + row of the 128-K step, bytes 4c .. 4c+3
-        *reinterpret_cast<uint32_t*>(codes + code_chunk(m / 16, kb / 4, K2, (kb & 3) * 16 + r) + c * 4) = cw;
-        if (c == (kb & 3)) scales[mx_scale_byte(m, kb, K2)] = uint8_t(sb);
-        if (R16 > 0) {
-          // down projection: x_hat as a bf16 hi + lo pair against the stored L1' fragments
+        const _Float16 h16 = (_Float16)fminf(amax / 7.0f, 65504.0f);
+        const float sc = (float)h16;
+        const float rs = 1.0f / sc;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t[e] = FAST ? div_refined(x[8 * h + e], sc, rs) : x[8 * h + e] / sc;
+          uint32_t cw = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float tq = __builtin_rintf(fminf(fmaxf(t[e], -8.0f), 7.0f));
+            const int q = (sc == 0.0f) ? 0 : int(tq);
+            cw |= (uint32_t(q) & 0xFu) << (8 * (e & 3) + 4 * (e >> 2));  // INT4 dword order
+          }
+          // group offset o = 32h + 8c: lane chunk (o / 16) * 16 + row, bytes 8 (g % 2) + (o % 16) / 2
+          *reinterpret_cast<uint32_t*>(codes + code_chunk(m / 16, kg / 2, K2, (2 * h + c / 2) * 16 + r) +
+                                       (kg & 1) * 8 + (c & 1) * 4) = cw;
+        }
+        if (c == 0) *reinterpret_cast<_Float16*>(scales + i4_scale_byte(m, kg, g.M_pad)) = h16;
+      }
+      if (R16 > 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // down projection: x_hat as a bf16 hi + lo pair against the next layer's L1 fragments
           uint4 hi, lo;
           hi.x = cvt_bf2(x[8 * h + 0], x[8 * h + 1]);
           hi.y = cvt_bf2(x[8 * h + 2], x[8 * h + 3]);
@@ -312,7 +345,7 @@ __device__ __forceinline__ void quant_rows(const GemmArgs& g, const uint8_t* slo
 // magnitude (the activation kernel's conditions); a first pass over the wave's
 // rows checks the values, and a wave with any value outside takes IEEE division
 // for all of its rows (same quotients, slower).
-template <int WN, int R16>
+template <int WN, int R16, int NFMT = kFmtMXFP4>
 __device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, int rbase, const float* lamv, int lane,
                                         int64_t mrow0, int k0, int tn, const uint4 (&l1r)[WN][R16 > 0 ? R16 : 1]) {
   const int r = lane & 15, c = lane >> 4;
@@ -327,9 +360,9 @@ __device__ __forceinline__ void quant_h(const GemmArgs& g, const uint8_t* slot, 
                        *reinterpret_cast<const uint4*>(slot + htile_off<WN>(rbase + t * 16 + r, s * 64 + 32 + c * 8)));
   const bool fast = (wf & (kLamRangeBit | kDivSlowBit)) == 0 && !__any(oor);
   if (__builtin_expect(fast, 1))
-    quant_rows<WN, R16, true>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
+    quant_rows<WN, R16, true, NFMT>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
   else
-    quant_rows<WN, R16, false>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
+    quant_rows<WN, R16, false, NFMT>(g, slot, rbase, lamv, lane, mrow0, k0, tn, l1r);
 }
 
 // Fused QKV epilogue (the next row after the layer: the Nunchaku in Diffusers
@@ -744,8 +777,11 @@ struct Int4Stage {
   uint32_t sx[WM];        // activation scales: the lane's row x 2 groups (fp16)
 };
 
-template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false>
+// QOUT >= 0: the fused MLP step (the output quantized for an INT4 next layer with
+// QOUT rank tiles of 16), as in the MXFP4 kernel's 128 x 128 tiles.
+template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false, int QOUT = -1>
 __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
+  static_assert(QOUT < 0 || (WN == 4 && WM == 4 && !OUT_F32 && !QKV), "fused MLP epilogue on 128 x 128 tiles");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
@@ -826,15 +862,41 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
     load(ks + 2 < KS ? ks + 2 : KS - 1, s0);
     compute(s1);
   }
-  __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
-  if constexpr (QKV) {
-    static_assert(!OUT_F32 && !GELU, "the QKV epilogue stores bf16 with no activation");
+  if constexpr (QOUT >= 0) {
+    // H = bf16(act(acc + b)) into LDS (two 64-row slots of the tile's 128
+    // columns), then each wave quantizes 32 of its rows for the next layer
+    __shared__ uint4 hs0[64 * 16], hs1[64 * 16];
+    __shared__ float lamv[3 * BN];
+    const int wn = w & 1, wm = w >> 1;
+    if (int(threadIdx.x) < BN) {
+      const int k = int(threadIdx.x);
+      const int64_t kn = int64_t(tn) * BN + k;
+      lamv[k] = reinterpret_cast<const float*>(g.nblob + g.n_lam)[kn];
+      lamv[BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlam)[kn];
+      lamv[2 * BN + k] = reinterpret_cast<const float*>(g.nblob + g.n_rlo)[kn];
+    }
     add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
-    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, stage + w * 32 * stage_row_bytes<WN>());
+    uint4 l1r[WN][QOUT > 0 ? QOUT : 1];
+    load_l1_next<QOUT, WN>(g, tn * BN, lane, l1r);
+    stage_h<WN, WM, GELU>(acc, bv, lane, wn, wm, reinterpret_cast<uint8_t*>(hs0), reinterpret_cast<uint8_t*>(hs1),
+                          nullptr, nullptr);
+    __syncthreads();
+    const int prow = w * 8 * WM;                     // the wave's first row of the tile
+    quant_h<WN, QOUT, kFmtINT4>(g, reinterpret_cast<const uint8_t*>(prow < 64 ? hs0 : hs1), prow & 63, lamv, lane,
+                                int64_t(tm) * BM + prow, tn * BN, tn, l1r);
   } else {
-    epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+    __shared__ uint8_t stage[4 * 32 * stage_row_bytes<WN>()];     // 32 rows per wave (store_out)
+    if constexpr (QKV) {
+      static_assert(!OUT_F32 && !GELU, "the QKV epilogue stores bf16 with no activation");
+      add_lowrank<WN, WM>(g, acc, n0, m0, lane);
+      float bv[WN][4];
+      load_bias<WN>(g, n0, lane, bv);
+      store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, stage + w * 32 * stage_row_bytes<WN>());
+    } else {
+      epilogue<WN, WM, OUT_F32, GELU>(g, acc, n0, m0, lane, stage + w * 32 * stage_row_bytes<WN>());
+    }
   }
 }
 
@@ -1356,11 +1418,12 @@ hipError_t launch_gemm_qkv(int fmt, const uint8_t* wblob, const WeightLayout& wl
   return hipGetLastError();
 }
 
-// The GEMM of one layer with its bf16 output quantized for the next layer (MXFP4
-// both), then the sum of the down-projection partials into that layer's D.
-hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act, const ActLayout& al,
-                             int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob, const WeightLayout& nwl,
-                             uint8_t* nact, const ActLayout& nal, hipStream_t s) {
+// The GEMM of one layer with its bf16 output quantized for the next layer (both
+// MXFP4 or both INT4), then the sum of the down-projection partials into that
+// layer's D.
+hipError_t launch_gemm_quant(int fmt, const uint8_t* wblob, const WeightLayout& wl, const uint8_t* act,
+                             const ActLayout& al, int K, int N, int64_t M, uint32_t epi, const uint8_t* nblob,
+                             const WeightLayout& nwl, uint8_t* nact, const ActLayout& nal, hipStream_t s) {
   GemmArgs g{};
   g.wblob = wblob;
   g.act = act;
@@ -1379,12 +1442,15 @@ hipError_t launch_gemm_quant(const uint8_t* wblob, const WeightLayout& wl, const
   // them, else 128 x 128 tiles (two workgroups per CU, so that one's
   // quantization overlaps the other's main loop).
   const unsigned big = unsigned((wl.N_pad / 256) * (al.M_pad / 256));
-  const bool bigt = use_big_tiles(big);
+  const bool int4 = fmt == kFmtINT4;                // the INT4 GEMM: 128 x 128 tiles only
+  const bool bigt = !int4 && use_big_tiles(big);
   const unsigned nb = bigt ? big : big * 4;
   const int tile_cols = bigt ? 256 : 128;
   const bool gelu = (epi & SVDQ_EPI_GELU) != 0;
 #define SVDQ_QLAUNCH(R16)                                                                                        \
-  if (bigt && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
+  if (int4 && gelu) hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, true, false, R16>), dim3(nb), dim3(256), 0, s, g); \
+  else if (int4) hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, false, false, R16>), dim3(nb), dim3(256), 0, s, g); \
+  else if (bigt && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
   else if (bigt) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, R16>), dim3(nb), dim3(256), 0, s, g);  \
   else if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, true, R16>), dim3(nb), dim3(256), 0, s, g);   \
   else hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, R16>), dim3(nb), dim3(256), 0, s, g)
