@@ -29,10 +29,16 @@
  *                   when S == 0.  Value = E2M1 * E4M3 * gs.
  * All float32 decision arithmetic is IEEE (correctly rounded divisions).
  *
- * Two launches per layer, as section 4.3 describes: svdq_quantize_act (smooth,
+ * Two steps per layer, as section 4.3 describes: svdq_quantize_act (smooth,
  * group amax, scale, encode, pack, and the down projection X_hat L1 in the same
  * pass over X) and svdq_gemm (the block-scaled 4-bit GEMM whose epilogue adds
- * (X_hat L1) L2, the bias and the activation).  svdq_linear runs both.
+ * (X_hat L1) L2, the bias and the activation).  svdq_linear runs both.  The
+ * quantize step is one kernel when it keeps K whole; when it splits K over
+ * workgroups to fill the GPU (every FLUX shape: 12 splits at K = 3072 and at
+ * K = 12288 for 4608 rows) a second small kernel sums the fp32 partials of the
+ * down projection in split order, so a layer is then three launches (the sum
+ * takes about 5 us at those shapes).  svdq_gemm_quant likewise ends with the
+ * sum of one partial per output tile column.
  *
  * Conventions for every entry point:
  *   - Pointers named as device buffers are device pointers owned by the caller;
@@ -46,7 +52,8 @@
  *     load-time capability check the Diffusers integration page describes).
  *   - No C++ exception crosses the ABI.  Calls that overlap on one stream are
  *     ordered; the library holds no mutable state (apart from a per-device
- *     cache of the architecture check) and is re-entrant.
+ *     cache of the architecture check, and svdq_linear_noalloc's static device
+ *     workspace, see there) and is re-entrant.
  *
  * Shapes: K % 512 == 0, 16 <= N, N % 16 == 0, 0 <= rank <= 256, M >= 0,
  * K <= 65536, N <= 65536.  Row strides (ldx, ldy) are in elements and
