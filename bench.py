@@ -17,8 +17,9 @@ activations times INT4 weights, the memory-bound modulation projection) and
 `roofline` is HBM-bound: algorithmic bytes (codes, scales, X, Y, bias) per
 launch over its event-timed duration.
 For the MXFP4 and INT4 pairs, `fused_mlp` times the same pair with fc1's GEMM quantizing
-its output for fc2 in its epilogue (svdq_gemm_quant: three launches plus the
-down-projection sum instead of four), same inputs, same step count.
+its output for fc2 in its epilogue (svdq_gemm_quant: three calls instead of four), same
+inputs and step count, with no event inside its timed steps either (its per-launch
+times come from a second pass); `fused_qkv` likewise for svdq_gemm_qkv.
 
 Operands (--operands): "calibrated" (default) converts each workload's dense
 seeded draw the way the SVDQuant notes page, section 4.2, makes a layer
@@ -30,7 +31,8 @@ GELU(X W1 + b1).  "drawn" takes synth.draw_layer's look-alike operands.
 `cold` repeats the timed loop over three or more copies of every operand,
 workspace and output (more bytes than the 256 MB last-level cache), so each
 step reads its operands from HBM; `repeats` gives the median of five more hot
-runs of the same loop; `clock` is what rocm-smi reports before and after.
+runs of the same loop; `clock` is the shader clock level the driver's sysfs file
+(pp_dpm_sclk) marks as current before and after.
 """
 from __future__ import annotations
 
@@ -619,6 +621,27 @@ def _blas_threads():
         return 1
 
 
+def _timed_then_breakdown(args, torch, step, n_launch):
+    """Warmup, then `steps` steps timed by the host clock with no event inside
+    the loop (as the main timed region), then the same steps again with events
+    around every launch for the per-launch breakdown (microseconds)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_launch + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    seg = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) * 1e3 / args.steps
+           for i in range(n_launch)]
+    return ms, seg
+
+
 def fused_qkv(args, sq, synth, torch, np, layer, w, x, ws, out, epi, M, flops):
     """The QKV layer with the Q/K RMS normalization and rotary embedding in the
     GEMM epilogue (svdq_gemm_qkv), same inputs and step count."""
@@ -636,17 +659,7 @@ def fused_qkv(args, sq, synth, torch, np, layer, w, x, ws, out, epi, M, flops):
         if ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    seg = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) * 1e3 / args.steps
-           for i in range(2)]
+    ms, seg = _timed_then_breakdown(args, torch, step, 2)
     return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
             "quantize_us": round(seg[0], 2), "gemm_qkv_us": round(seg[1], 2),
             "launches": "quantize_act; gemm_qkv (GEMM with Q/K RMS norm and rotary embedding in the epilogue)"}
@@ -667,17 +680,7 @@ def fused_pair(args, sq, torch, layers, weights, x, ws, outs, epis, M, flops):
         if ev is not None:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    seg = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)) * 1e3 / args.steps
-           for i in range(3)]
+    ms, seg = _timed_then_breakdown(args, torch, step, 3)
     return {"value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
             "fc1_quantize_us": round(seg[0], 2), "fc1_gemm_quant_us": round(seg[1], 2),
             "fc2_gemm_us": round(seg[2], 2),
