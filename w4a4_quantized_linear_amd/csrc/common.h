@@ -101,15 +101,15 @@ __device__ __forceinline__ v4i mfma_i8(const v4i& a, const v4i& b) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, z, 0, 0, 0);
 }
 
-// 8 packed two's complement nibbles -> 8 signed bytes in two dwords (the low
-// nibbles of the 4 bytes in the first, the high nibbles in the second; in the
-// INT4 code order these are codes 0-3 and 4-7).  Per byte, with x the nibble:
-// ((x ^ 8) + 0x78) ^ 0x80 is x sign-extended, with no carry between bytes.
-__device__ __forceinline__ void unpack_i4x8(uint32_t d, int& first, int& second) {
-  const uint32_t lo = d & 0x0F0F0F0Fu;
-  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;
-  first = int(((lo ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
-  second = int(((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
+// 8 packed two's complement nibbles -> 8 signed bytes, each 16 times its code,
+// in two dwords (the low nibbles of the 4 bytes in the first, the high nibbles
+// in the second; in the INT4 code order these are codes 0-3 and 4-7).  A
+// nibble moved to the top of its byte is its code times 16 as a signed byte, so
+// this is one mask per dword and a shift: an int8 product of two such operands
+// is 256 times the codes' product, exactly.
+__device__ __forceinline__ void unpack_i4x8_x16(uint32_t d, int& first, int& second) {
+  first = int((d << 4) & 0xF0F0F0F0u);
+  second = int(d & 0xF0F0F0F0u);
 }
 
 // 8 packed bf16 -> fp32, element order kept

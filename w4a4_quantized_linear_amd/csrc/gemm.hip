@@ -750,13 +750,14 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
 
 __device__ __forceinline__ float h2f(uint32_t bits) { return float(__builtin_bit_cast(_Float16, uint16_t(bits))); }
 
+// A fragment's 32 codes as int8 operands of two 64-K MFMAs, each code times 16.
 __device__ __forceinline__ void unpack_frag(const uint4& q, v4i& g0, v4i& g1) {
   int e0, o0, e1, o1;
-  unpack_i4x8(q.x, e0, o0);
-  unpack_i4x8(q.y, e1, o1);
+  unpack_i4x8_x16(q.x, e0, o0);
+  unpack_i4x8_x16(q.y, e1, o1);
   g0 = v4i{e0, o0, e1, o1};
-  unpack_i4x8(q.z, e0, o0);
-  unpack_i4x8(q.w, e1, o1);
+  unpack_i4x8_x16(q.z, e0, o0);
+  unpack_i4x8_x16(q.w, e1, o1);
   g1 = v4i{e0, o0, e1, o1};
 }
 
@@ -782,7 +783,8 @@ struct Int4Stage {
 template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false, int QOUT = -1>
 __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   static_assert(QOUT < 0 || (WN == 4 && WM == 4 && !OUT_F32 && !QKV), "fused MLP epilogue on 128 x 128 tiles");
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
   int tm, tn;
@@ -791,24 +793,33 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
   const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
   const int KS = g.K / kKStep;
 
-  const uint4* Wc = reinterpret_cast<const uint4*>(g.wblob + g.w_codes) + (n0 / 16) * KS * 64 + lane;
-  const uint4* Ac = reinterpret_cast<const uint4*>(g.act + g.a_codes) + (m0 / 16) * KS * 64 + lane;
-  // scales: [ks][rows_pad][2] fp16
-  const uint4* Wsc = reinterpret_cast<const uint4*>(g.wblob + g.w_scales);
-  const uint32_t* Asc = reinterpret_cast<const uint32_t*>(g.act + g.a_scales);
-  const int64_t wrow = n0 + (lane >> 4) * 4;  // first of the lane's 4 weight rows in block 0
-  const int64_t arow = m0 + (lane & 15);
+  // Buffer views: the wave's WN weight and WM activation row tiles of codes,
+  // and the scales ([ks][rows_pad][2] fp16); lane offsets in the vector
+  // operand, the step's offsets in the scalar one (no per-load address math).
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(g.wblob + g.w_codes + size_t(n0 / 16) * KS * 1024, uint32_t(WN) * KS * 1024);
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(g.act + g.a_codes + size_t(m0 / 16) * KS * 1024, uint32_t(WM) * KS * 1024);
+  // (weight scales: at most 512 steps x 65536 rows x 4 bytes, within 32 bits;
+  // activation scales, with up to 2^26 rows: one view per step)
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(g.wblob + g.w_scales, uint32_t(KS * g.N_pad * 4));
+  const uint32_t voff16 = uint32_t(lane) * 16;
+  const uint32_t wsoff = uint32_t(n0 + (lane >> 4) * 4) * 4;   // the lane's 4 weight rows in block 0
+  const uint32_t xsoff = uint32_t(m0 + (lane & 15)) * 4;
 
   auto load = [&](int ks, Int4Stage<WN, WM>& st) {
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      st.cw[i] = Wc[(size_t(i) * KS + ks) * 64];
-      st.sw[i] = Wsc[(size_t(ks) * g.N_pad + wrow + i * 16) / 4];  // 4 rows x 2 fp16 per 16 B
+      st.cw[i] = load_frag(rW, voff16, uint32_t(i * KS + ks) * 1024);
+      const v4i sv = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rWs, wsoff, uint32_t(ks * g.N_pad + i * 16) * 4, 0));
+      st.sw[i] = make_uint4(uint32_t(sv[0]), uint32_t(sv[1]), uint32_t(sv[2]), uint32_t(sv[3]));
     }
+    const __amdgpu_buffer_rsrc_t rXs = make_rsrc(g.act + g.a_scales + size_t(ks) * g.M_pad * 4, uint32_t(g.M_pad * 4));
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
-      st.cx[j] = Ac[(size_t(j) * KS + ks) * 64];
-      st.sx[j] = Asc[size_t(ks) * g.M_pad + arow + j * 16];
+      st.cx[j] = load_frag(rX, voff16, uint32_t(j * KS + ks) * 1024);
+      st.sx[j] = __builtin_amdgcn_raw_buffer_load_b32(rXs, xsoff, uint32_t(j * 16) * 4, 0);
     }
   };
 
@@ -862,6 +873,18 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
     load(ks + 2 < KS ? ks + 2 : KS - 1, s0);
     compute(s1);
   }
+  // Both MFMA operands carry a factor 16 (unpack_frag), so every int32 sum is
+  // 256 times the codes' sum (|sum| <= 2^20, exact as a float) and so is every
+  // accumulator: each FMA adds 256 times the term to 256 times the sum, which
+  // rounds to exactly 256 times the unscaled result (every nonzero partial sum
+  // is at least 2^-48, a product of two fp16 scales, far from fp32 underflow).
+  // One exact scaling by 2^-8 gives the same bits as unscaled operands.
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] *= 0x1p-8f;
   if constexpr (QOUT >= 0) {
     // H = bf16(act(acc + b)) into LDS (two 64-row slots of the tile's 128
     // columns), then each wave quantizes 32 of its rows for the next layer
