@@ -7,9 +7,9 @@ on synthetic seeded inputs already resident in HBM (weights packed once before
 timing, as at load time).  value = (2 M N K of fc1 + of fc2) per step / time.
 
 Prints one JSON line.  `roofline` is the fc1 GEMM kernel (the dominant launch),
-timed with HIP events around each of its launches inside the timed region (the
-only markers there); `breakdown` times every launch with events in a second,
-untimed pass.  Before the warmup steps the same steps run untimed for
+timed with HIP events around its launches in every --roofline-every-th step of
+the timed region (the only markers there; each marker adds a small gap to the
+stream); `breakdown` times every launch with events in a second, untimed pass.  Before the warmup steps the same steps run untimed for
 --settle-ms so that the shader clock has left its idle level.
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 With --workload mod_w4a16 the step is one W4A16 launch (svdq_gemm_w4a16: bf16
@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--operands", default="calibrated", choices=["calibrated", "drawn"],
                    help="layer operands: converted from the dense draw (default) or drawn look-alikes")
     p.add_argument("--no-cold", action="store_true", help="skip the cold (operand-rotating) timing")
+    p.add_argument("--roofline-every", type=int, default=5, metavar="N",
+                   help="events around the roofline GEMM in every N-th timed step (default 5)")
     p.add_argument("--settle-ms", type=float, default=300.0,
                    help="run untimed steps for this long before the warmup, so the shader clock has ramped up")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -396,19 +398,23 @@ def gpu_leg(args, ops):
         torch.cuda.synchronize()
         del src, dst
 
-    # Timed region: exactly `steps` steps, events only around the roofline GEMM.
-    dom = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps; the only markers are a pair of events
+    # around the roofline GEMM in every `roofline_every`-th step (each marker
+    # adds a gap to the stream, so fewer of them keep the step time clean).
+    every = max(1, args.roofline_every)
+    sampled = list(range(0, args.steps, every))
+    dom = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in sampled}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        step(dom_ev=dom[k])
+        step(dom_ev=dom.get(k))
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
-    dom_us = sum(dom[k][0].elapsed_time(dom[k][1]) for k in range(args.steps)) * 1e3 / args.steps
+    dom_us = sum(dom[k][0].elapsed_time(dom[k][1]) for k in sampled) * 1e3 / len(sampled)
     flops = [2.0 * M * s.N * s.K for s in specs]
     ms_per_step = wall * 1e3 / args.steps
     value = sum(flops) / (ms_per_step * 1e-3) / 1e12
@@ -429,7 +435,8 @@ def gpu_leg(args, ops):
     kname = f"gemm_{fmt}_{specs[i_dom].name}"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(kname, args.workload),
-                "kernel": kname, "flops_per_launch": flops[i_dom], "avg_launch_us": round(dom_us, 2)}
+                "kernel": kname, "flops_per_launch": flops[i_dom], "avg_launch_us": round(dom_us, 2),
+                "launches_timed": len(sampled)}
     breakdown = {}
     for i, s in enumerate(specs):
         hbm_q = 2 * M * s.K + M * s.K // 2 + M * s.K // 32 + 4 * M * layers[i].rank + 2 * s.K * layers[i].rank
