@@ -968,7 +968,8 @@ struct Nv4Stage {
 
 template <int WN, int WM, bool OUT_F32, bool GELU, bool QKV = false>
 __global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   constexpr int BN = 2 * WN * 16, BM = 2 * WM * 16;
   const int tiles_m = int(g.M_pad / BM);
   int tm, tn;
@@ -977,22 +978,29 @@ __global__ void __launch_bounds__(256, 2) gemm_nvfp4_kernel(GemmArgs g) {
   const int64_t m0 = int64_t(tm) * BM + (w >> 1) * (WM * 16);
   const int KS = g.K / kKStep;
 
-  const uint4* Wc = reinterpret_cast<const uint4*>(g.wblob + g.w_codes) + (n0 / 16) * KS * 64 + lane;
-  const uint4* Ac = reinterpret_cast<const uint4*>(g.act + g.a_codes) + (m0 / 16) * KS * 64 + lane;
-  // scales: per 16-row tile and step, lane L's two bytes at 2 L
-  const uint16_t* Wsc = reinterpret_cast<const uint16_t*>(g.wblob + g.w_scales) + (n0 / 16) * KS * 64 + lane;
-  const uint16_t* Asc = reinterpret_cast<const uint16_t*>(g.act + g.a_scales) + (m0 / 16) * KS * 64 + lane;
+  // Buffer views of the wave's WN weight and WM activation row tiles: codes
+  // (1 KiB per tile and step) and scales (per tile and step, lane L's two bytes
+  // at 2 L); lane offsets in the vector operand, step offsets in the scalar one.
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(g.wblob + g.w_codes + size_t(n0 / 16) * KS * 1024, uint32_t(WN) * KS * 1024);
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(g.act + g.a_codes + size_t(m0 / 16) * KS * 1024, uint32_t(WM) * KS * 1024);
+  const __amdgpu_buffer_rsrc_t rWs =
+      make_rsrc(g.wblob + g.w_scales + size_t(n0 / 16) * KS * 128, uint32_t(WN) * KS * 128);
+  const __amdgpu_buffer_rsrc_t rXs =
+      make_rsrc(g.act + g.a_scales + size_t(m0 / 16) * KS * 128, uint32_t(WM) * KS * 128);
+  const uint32_t voff16 = uint32_t(lane) * 16, voff2 = uint32_t(lane) * 2;
 
   auto load = [&](int ks, Nv4Stage<WN, WM>& st) {
 #pragma unroll
     for (int i = 0; i < WN; ++i) {
-      st.cw[i] = Wc[(size_t(i) * KS + ks) * 64];
-      st.sw[i] = Wsc[(size_t(i) * KS + ks) * 64];
+      st.cw[i] = load_frag(rW, voff16, uint32_t(i * KS + ks) * 1024);
+      st.sw[i] = __builtin_amdgcn_raw_buffer_load_b16(rWs, voff2, uint32_t(i * KS + ks) * 128, 0);
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
-      st.cx[j] = Ac[(size_t(j) * KS + ks) * 64];
-      st.sx[j] = Asc[(size_t(j) * KS + ks) * 64];
+      st.cx[j] = load_frag(rX, voff16, uint32_t(j * KS + ks) * 1024);
+      st.sx[j] = __builtin_amdgcn_raw_buffer_load_b16(rXs, voff2, uint32_t(j * KS + ks) * 128, 0);
     }
   };
 

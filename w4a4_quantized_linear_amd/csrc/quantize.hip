@@ -204,14 +204,30 @@ __global__ void __launch_bounds__(64 * kActRowTiles, act_min_waves(R16)) quantiz
   uint4 xs[kActDepth + 1][2];
 #pragma unroll
   for (int j = 0; j < kActDepth; ++j) load_x(j, xs[j][0], xs[j][1]);
-  for (int i = threadIdx.x; i < kr / 4; i += blockDim.x) {
-    reinterpret_cast<float4*>(slam)[i] = reinterpret_cast<const float4*>(lam + k_beg)[i];
-    reinterpret_cast<float4*>(srlam)[i] = reinterpret_cast<const float4*>(rlam + k_beg)[i];
-    reinterpret_cast<float4*>(srlo)[i] = reinterpret_cast<const float4*>(rlo + k_beg)[i];
+  // The staging is done by loads that write LDS directly: no register round
+  // trip, every chunk in flight at once (a copy through registers waits for
+  // each load in turn); the barrier's wait covers them.  lambda, 1/lambda and
+  // the correction: kr / 64 chunks of 256 bytes each.
+  {
+    const int nl = kr / 64;
+    const __amdgpu_buffer_rsrc_t rl0 = make_rsrc(lam + k_beg, uint32_t(kr) * 4);
+    const __amdgpu_buffer_rsrc_t rl1 = make_rsrc(rlam + k_beg, uint32_t(kr) * 4);
+    const __amdgpu_buffer_rsrc_t rl2 = make_rsrc(rlo + k_beg, uint32_t(kr) * 4);
+    for (int ci = w; ci < 3 * nl; ci += kActRowTiles) {
+      const int a = ci / nl, o = ci % nl;
+      float* const dst = (a == 0 ? slam : a == 1 ? srlam : srlo) + o * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a == 0 ? rl0 : a == 1 ? rl1 : rl2,
+                                               (__attribute__((address_space(3))) void*)(dst), 4,
+                                               uint32_t(lane) * 4, uint32_t(o) * 256, 0, 0);
+    }
   }
   if (R16 > 0) {
-    const uint4* src = L1f + size_t(k_beg / 32) * R16 * 64;
-    for (int i = threadIdx.x; i < (kr / 32) * R16 * 64; i += blockDim.x) sl1[i] = src[i];
+    // the L1 fragments of this K range: (kr / 32) R16 chunks of 1 KiB
+    const int nchunk = (kr / 32) * R16;
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(L1f + size_t(k_beg / 32) * R16 * 64, uint32_t(nchunk) * 1024);
+    for (int ci = w; ci < nchunk; ci += kActRowTiles)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl1 + ci * 64), 16,
+                                               uint32_t(lane) * 16, uint32_t(ci) * 1024, 0, 0);
   }
   __syncthreads();
 
