@@ -229,6 +229,42 @@ def test_edge_values_bit_exact(torch_dev, fmt):
     assert np.all(np.isfinite(Y.cpu().numpy()))
 
 
+def test_int4_largest_group_sums(torch_dev):
+    """INT4 operands whose every row is one value up to sign (codes all 7 in
+    magnitude): each 64-group's integer sum reaches the largest magnitude the
+    quantizer can give, 64 * 49, or cancels to 0.  The GEMM's int8 operands hold
+    16 times the codes, so its int32 sums are 256 times these; the codes and the
+    output still match the oracle."""
+    torch, dev = torch_dev
+    M, K, N = 64, 1024, 64
+    spec = synth.layer_spec("single", M=M, K=K, N=N, rank=0, fmt="int4", x_outliers=1, w_outliers=1, lora_rank=0)
+    L = synth.draw_layer(spec, seed=31)
+    k = np.arange(K)
+    alt = np.where(k % 2 == 0, 1.0, -1.0)
+    # X rows: +c, -c, or c alternating in sign along K; R rows likewise
+    X = np.empty((M, K), np.float32)
+    for m in range(M):
+        pat = (np.ones(K), -np.ones(K), alt)[m % 3]
+        X[m] = pat * (0.5 + 0.25 * m)
+    R = np.empty((N, K), np.float32)
+    for n in range(N):
+        pat = (np.ones(K), alt, -alt)[n % 3]
+        R[n] = pat * (1.0 + 0.125 * n)
+    L["X"] = synth.bf16_bits_from_f32(X)
+    L["R"] = R
+    L["lam"] = np.ones(K, np.float32)
+    layer = sq.Layer("int4", K, N, 0)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    ua = sq.unpack_act(layer, ws, M)
+    Y = sq.gemm(layer, w, ws, M, sq.EPI_BIAS | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "int4")
+    assert np.abs(ref["cX"].astype(np.int64)).max() == 7, "codes of the largest magnitude"
+    assert_codes_equal(ua["codes"].cpu().numpy(), ref["cX"], "activation codes")
+    check_fp32_output(Y.cpu().numpy(), ref["Y"], "largest INT4 group sums")
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4", "nvfp4"])
 @pytest.mark.parametrize("lam_edge", ["inside", "outside"])
 def test_division_range_edges_bit_exact(torch_dev, fmt, lam_edge):
