@@ -180,6 +180,31 @@ def test_short_tiles_elementwise(torch_dev):
         check_bf16_output(bf16_to_np(Yg), Ly.gelu(ref["Y"]), f"M={M} N={N} GELU bf16")
 
 
+@pytest.mark.parametrize("M,K,N,rank,seed", [(1000, 3072, 1008, 128, 46), (257, 4096, 400, 32, 47),
+                                              (2048, 1024, 2048, 16, 48), (33, 2048, 3072, 100, 49)],
+                         ids=["64-tiles-K3072-r128", "12-tiles-K4096", "256-tiles-K1024", "24-tiles-K2048-r100"])
+def test_one_tile_per_cu_elementwise(torch_dev, M, K, N, rank, seed):
+    """MXFP4 grids of at most one 128 x 128 tile per CU (the low-M shape's
+    schedule) with long K: 24 to 32 K steps, ragged M and N, ranks up to 128,
+    exactly 256 tiles.  fp32, bf16 and GELU outputs element by element against
+    the oracle; bf16 must be the round-to-nearest-even of fp32."""
+    torch, dev = torch_dev
+    spec, L = _medium_layer("lowm", "mxfp4", M, K, N, rank, seed)
+    layer = sq.Layer("mxfp4", K, N, rank)
+    print(f"one tile per CU M={M} K={K} N={N} rank={rank}", flush=True)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    Yf = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    Yb = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS)
+    Yg = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU | sq.EPI_OUT_F32)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")
+    check_fp32_output(Yf.cpu().numpy(), ref["Y"], f"M={M} K={K} N={N} fp32")
+    check_bf16_output(bf16_to_np(Yb), ref["Y"], f"M={M} K={K} N={N} bf16")
+    assert np.array_equal(Yb.cpu().view(torch.int16).numpy().view(np.uint16), F.bf16_bits(Yf.cpu().numpy()))
+    check_fp32_output(Yg.cpu().numpy(), Ly.gelu(ref["Y"]), f"M={M} K={K} N={N} GELU")
+
+
 def test_gelu_epilogue_pointwise(torch_dev):
     """The GEMM's GELU against the exact erf form, value by value: with R = 0,
     rank 0 and lambda = 1 the output is GELU(b), so the bias carries the test
