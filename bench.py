@@ -735,8 +735,8 @@ def main():
         return
     if args.traffic_from:
         t = traffic_from(*args.traffic_from)
-        names = {"gemm_mxfp4_kernel<4, 4, false, true, -1, false, 4>": "mlp_mxfp4:gemm_mxfp4_fc1_mxfp4",
-                 "gemm_mxfp4_kernel<8, 8, false, false, -1, false, 7>": "mlp_mxfp4:gemm_mxfp4_fc2_mxfp4"}
+        names = {"gemm_mxfp4_kernel<4, 4, false, true, -1, false, 4, 3>": "mlp_mxfp4:gemm_mxfp4_fc1_mxfp4",
+                 "gemm_mxfp4_kernel<8, 8, false, false, -1, false, 7, 4>": "mlp_mxfp4:gemm_mxfp4_fc2_mxfp4"}
         d = {names[k]: dict(v, gemm_source_sha256_16=gemm_source_hash()) for k, v in t.items() if k in names}
         with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
             json.dump(d, f, indent=1)

@@ -205,6 +205,35 @@ def test_one_tile_per_cu_elementwise(torch_dev, M, K, N, rank, seed):
     check_fp32_output(Yg.cpu().numpy(), Ly.gelu(ref["Y"]), f"M={M} K={K} N={N} GELU")
 
 
+@pytest.mark.parametrize("M,K,N,rank,seed", [(2100, 1536, 4000, 48, 50), (1100, 3072, 8208, 32, 51)],
+                         ids=["544-tiles-K1536-r48", "585-tiles-K3072"])
+def test_three_per_cu_elementwise(torch_dev, M, K, N, rank, seed):
+    """MXFP4 grids of more than two 128 x 128 tiles per CU with K a multiple of
+    1536 take the three-slot ring (three workgroups per CU, blocks of twelve
+    128-K steps whose last two loads read nothing): one and two blocks, ragged M
+    and N.  fp32, bf16, bias-free bf16 and GELU outputs element by element
+    against the oracle; bf16 must be the round-to-nearest-even of fp32 (the
+    bf16 stores are staged through the ring after the loop)."""
+    torch, dev = torch_dev
+    spec, L = _medium_layer("qkv", "mxfp4", M, K, N, rank, seed)
+    layer = sq.Layer("mxfp4", K, N, rank)
+    print(f"three per CU M={M} K={K} N={N} rank={rank}", flush=True)
+    w = pack(layer, L, torch, dev)
+    ws = sq.quantize_act(layer, w, dev_tensor(L["X"], torch, dev))
+    Yf = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32)
+    Yb = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS)
+    Yn = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK)
+    Yg = sq.gemm(layer, w, ws, M, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU)
+    torch.cuda.synchronize()
+    ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4")
+    check_fp32_output(Yf.cpu().numpy(), ref["Y"], f"M={M} K={K} N={N} fp32")
+    check_bf16_output(bf16_to_np(Yb), ref["Y"], f"M={M} K={K} N={N} bf16")
+    assert np.array_equal(Yb.cpu().view(torch.int16).numpy().view(np.uint16), F.bf16_bits(Yf.cpu().numpy()))
+    ref_nb = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], "mxfp4", with_bias=False)
+    check_bf16_output(bf16_to_np(Yn), ref_nb["Y"], f"M={M} K={K} N={N} bf16 without bias")
+    check_bf16_output(bf16_to_np(Yg), Ly.gelu(ref["Y"]), f"M={M} K={K} N={N} GELU bf16")
+
+
 def test_gelu_epilogue_pointwise(torch_dev):
     """The GEMM's GELU against the exact erf form, value by value: with R = 0,
     rank 0 and lambda = 1 the output is GELU(b), so the bias carries the test

@@ -494,6 +494,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 // of another and adds no waits of its own.  The E8M0 scales of a 512-K
 // superfragment (one dword per lane and 16-row tile) are loaded one
 // superfragment ahead; the MFMA of step u of the superfragment picks byte u.
+// The 128 x 128 tiles also come with a three-slot ring (NS = 3, 48 KiB, three
+// workgroups per CU): there step t reads its own fragments first and loads
+// stage t+2 into the slot of stage t-1.
 
 
 __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -532,8 +535,11 @@ __device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int
   tm = in / gcols;
 }
 
-template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM>
-__global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmArgs g) {
+template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM, int NS = 4>
+__global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxfp4_kernel(GemmArgs g) {
+  // NS = 3: a three-slot ring (48 KiB) so that three workgroups share a CU;
+  // each step reads its own fragments at its start (plain 128 x 128 tiles).
+  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT < 0 && !QKV), "three-slot ring: plain 128 x 128 tiles");
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
@@ -542,7 +548,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
   constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
   static_assert(2 * PW == WN, "each wave row issues one fragment load per step");
-  __shared__ uint4 ring0[SU4], ring1[SU4], ring2[SU4], ring3[SU4];   // 4 x 32 KiB (8 x 8) or 4 x 16 KiB
+  __shared__ uint4 ring0[SU4], ring1[SU4], ring2[SU4], ring3[NS == 4 ? SU4 : 1];   // 4 x 32 KiB (8 x 8) or 4 x 16 KiB
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = w & 1, wm = w >> 1;               // 2 x 2 waves
@@ -558,7 +564,12 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
   const int KS = g.K / kKStep, KSUP = g.K / kKSuper;
   const int64_t n0 = (nt0 + wn * WN) * 16;
   const int64_t m0 = (mt0 + wm * WMA) * 16;
-  auto slot = [&](int u) -> uint4* { return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3; };
+  auto slot = [&](int u) -> uint4* {
+    if constexpr (NS == 3)
+      return u == 0 ? ring0 : u == 1 ? ring1 : ring2;
+    else
+      return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3;
+  };
 
   // Per-workgroup views of the operands: SF row tiles of codes and of scales each.
   // A stage always holds SF activation fragments; with short tiles the last
@@ -591,6 +602,15 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     const int fi = wt ? f : f - PW;
     const uint32_t so = uint32_t((PW * w + fi) * KS + step) * 1024;
     load_frag_lds(wt ? rA : rB, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
+  };
+  // The same, or (!valid) the same load through a buffer resource of zero
+  // bytes: every lane is out of range, so it writes zeros and reads no memory.
+  const __amdgpu_buffer_rsrc_t rZ = make_rsrc(g.wblob, 0u);
+  auto fetch1x = [&](uint4* dst_stage, int step, int f, bool valid) {
+    const bool wt = f < PW;
+    const int fi = wt ? f : f - PW;
+    const uint32_t so = uint32_t((PW * w + fi) * KS + step) * 1024;
+    load_frag_lds(valid ? (wt ? rA : rB) : rZ, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
   };
   auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
   auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WMA + j) * 64 + lane]; };
@@ -637,8 +657,10 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
 #pragma unroll
     for (int f = 0; f < 2 * PW; ++f) fetch1(ring1, 1, f);
+    if constexpr (NS == 4) {
 #pragma unroll
-    for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+      for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+    }
     if (lowrank) {
       lowrank_mfma(l2, dh, dl);
       for (int r32 = 1; r32 < R32; ++r32) {
@@ -647,17 +669,19 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
       }
     }
   }
-  wait_barrier<2 * PW>();                          // stages 0 and 1 are in LDS
+  wait_barrier<2 * PW>();                          // stages 0 and 1 (three slots: stage 0) are in LDS
   // Fragments in registers, reloaded in place.  A step runs its 8 x 8 MFMAs in
   // two halves by activation fragment: half 0 uses fb[0..3] and meanwhile reads
   // fb[4..7] of the same stage; half 1 uses fb[4..7] and meanwhile reads the
   // next stage's fb[0..3] and, after row i, fa[i].  So every fragment is read
   // while the MFMAs of another one run, and the reads spread over the step.
   uint4 fa[WN], fb[WMA];
+  if constexpr (NS == 4) {
 #pragma unroll
-  for (int j = 0; j < WM / 2; ++j) fb[j] = frag_b(ring0, j);
+    for (int j = 0; j < WM / 2; ++j) fb[j] = frag_b(ring0, j);
 #pragma unroll
-  for (int i = 0; i < WN; ++i) fa[i] = frag_a(ring0, i);
+    for (int i = 0; i < WN; ++i) fa[i] = frag_a(ring0, i);
+  }
 
   // Step U of a superfragment.  Row i also issues one fragment load of stage
   // step+3 (2 PW = WN loads per step).  The flags drop the loads / reads of stages past the end in the
@@ -693,25 +717,81 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     __builtin_amdgcn_sched_barrier(0);                                                                \
     wait_barrier<(VM)>();                                                                             \
   }
-  int sup = 0;
-  for (; sup + 1 < KSUP; ++sup) {
-    const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
-    SVDQ_FP4_STEP(1, true, true, true, 2 * PW + WN + WMA)
-    SVDQ_FP4_STEP(2, true, true, false, 2 * PW)
-    SVDQ_FP4_STEP(3, true, true, false, 2 * PW)
-#pragma unroll
-    for (int i = 0; i < WN; ++i) sa[i] = san[i];
-#pragma unroll
-    for (int j = 0; j < WMA; ++j) sb[j] = sbn[j];
+  // Three slots: step U (of twelve, three superfragments) reads its own
+  // fragments from slot U % 3 first, runs its MFMAs while issuing the loads of
+  // stage step+2 into slot (U+2) % 3 (which held stage step-1, read during the
+  // previous step), and at its end waits for stage step+1: what may still be in
+  // flight is stage step+2 and the scale loads issued after stage step+1's.
+  // Every block of twelve steps goes through the loop (a straight-line copy of
+  // the last block, or a branch around its loads, made the register allocator
+  // spill accumulators): in the last two steps the stage loads go through a
+  // buffer resource of zero bytes (they write zeros into slots already consumed
+  // and read no memory), and the last scale load repeats the last
+  // superfragment, so that the wait counts hold throughout.  The loop is
+  // followed by a wait for every load, so that those zeros have landed before
+  // the epilogue writes its LDS staging.
+#define SVDQ_FP4_STEP3(U, SCALES, VM)                                                                 \
+  {                                                                                                   \
+    const int step = t0 + (U);                                                                        \
+    const bool fv = step + 2 < KS;                                                                    \
+    uint4* const sf = slot(((U) + 2) % 3);                                                            \
+    const uint4* const sc = slot((U) % 3);                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                                \
+    _Pragma("unroll") for (int j = 0; j < WM; ++j) fb[j] = frag_b(sc, j);                             \
+    _Pragma("unroll") for (int i = 0; i < WN; ++i) fa[i] = frag_a(sc, i);                             \
+    _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
+      fetch1x(sf, step + 2, i, fv);                                                                   \
+      _Pragma("unroll") for (int j = 0; j < WM; ++j)                                                  \
+        acc[i][j] = mfma_fp4_sel<((U) & 3)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                   \
+      __builtin_amdgcn_sched_barrier(0);                                                              \
+    }                                                                                                 \
+    if (SCALES) load_scales(san, sbn, (step >> 2) + 1 < KSUP ? (step >> 2) + 1 : KSUP - 1);           \
+    __builtin_amdgcn_sched_barrier(0);                                                                \
+    wait_barrier<(VM)>();                                                                             \
+    if (((U) & 3) == 3) {                                                                             \
+      _Pragma("unroll") for (int i = 0; i < WN; ++i) sa[i] = san[i];                                  \
+      _Pragma("unroll") for (int j = 0; j < WMA; ++j) sb[j] = sbn[j];                                 \
+    }                                                                                                 \
   }
-  {
-    const int t0 = sup * 4;
-    SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
-    SVDQ_FP4_STEP(1, false, true, false, 0)
-    SVDQ_FP4_STEP(2, false, true, false, 0)
-    SVDQ_FP4_STEP(3, false, false, false, 0)
+  if constexpr (NS == 3) {
+    constexpr int F = 2 * PW, S = WN + WMA;        // loads per stage, per superfragment's scales
+    for (int t0 = 0; t0 < KS; t0 += 12) {
+      SVDQ_FP4_STEP3(0, false, F)
+      SVDQ_FP4_STEP3(1, true, F + S)
+      SVDQ_FP4_STEP3(2, false, F + S)
+      SVDQ_FP4_STEP3(3, false, F)
+      SVDQ_FP4_STEP3(4, false, F)
+      SVDQ_FP4_STEP3(5, true, F + S)
+      SVDQ_FP4_STEP3(6, false, F + S)
+      SVDQ_FP4_STEP3(7, false, F)
+      SVDQ_FP4_STEP3(8, false, F)
+      SVDQ_FP4_STEP3(9, true, F + S)
+      SVDQ_FP4_STEP3(10, false, F + S)
+      SVDQ_FP4_STEP3(11, false, F)
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the last block's re-fetch has landed
+  } else {
+    int sup = 0;
+    for (; sup + 1 < KSUP; ++sup) {
+      const int t0 = sup * 4;
+      SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
+      SVDQ_FP4_STEP(1, true, true, true, 2 * PW + WN + WMA)
+      SVDQ_FP4_STEP(2, true, true, false, 2 * PW)
+      SVDQ_FP4_STEP(3, true, true, false, 2 * PW)
+#pragma unroll
+      for (int i = 0; i < WN; ++i) sa[i] = san[i];
+#pragma unroll
+      for (int j = 0; j < WMA; ++j) sb[j] = sbn[j];
+    }
+    {
+      const int t0 = sup * 4;
+      SVDQ_FP4_STEP(0, true, true, false, 2 * PW)
+      SVDQ_FP4_STEP(1, false, true, false, 0)
+      SVDQ_FP4_STEP(2, false, true, false, 0)
+      SVDQ_FP4_STEP(3, false, false, false, 0)
+    }
   }
+#undef SVDQ_FP4_STEP3
 #undef SVDQ_FP4_STEP
   // every wave passed the last barrier with no load in flight: the ring is free
   // for the output staging (one slot per wave)
@@ -742,7 +822,10 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : 2) gemm_mxfp4_kernel(GemmAr
     load_bias<WN>(g, n0, lane, bv);
     store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
   } else {
-    epilogue<WN, WMA, OUT_F32, GELU, !LR_FIRST, (WMA < WM)>(g, acc, n0, m0, lane, reinterpret_cast<uint8_t*>(slot(w)));
+    // bf16 staging: 32 rows of stage_row_bytes per wave; two waves per slot with three slots
+    uint8_t* const stage = NS == 3 ? reinterpret_cast<uint8_t*>(slot(w >> 1)) + (w & 1) * 32 * stage_row_bytes<WN>()
+                                   : reinterpret_cast<uint8_t*>(slot(w));
+    epilogue<WN, WMA, OUT_F32, GELU, !LR_FIRST, (WMA < WM)>(g, acc, n0, m0, lane, stage);
   }
 }
 
@@ -1328,6 +1411,11 @@ static int device_cus() {
 // to one round of them on this device's CUs, else 128 x 128 tiles.
 static bool use_big_tiles(unsigned big) { return big >= kMinBigTiles && big < unsigned(device_cus()); }
 
+// MXFP4 128 x 128 tiles with the three-slot ring (three workgroups per CU) when
+// the grid is more than two workgroups per CU; its loop takes blocks of twelve
+// 128-K steps.
+static bool use_three_slots(unsigned tiles, int K) { return tiles > 2u * unsigned(device_cus()) && K % 1536 == 0; }
+
 // Height of the 256-wide tiles, as activation blocks of 16 rows per wave (the
 // tile is 32 wma rows): the fewest rounds of workgroups on the CUs times the
 // rows per tile, the taller tile on a tie.  FLUX fc2 (4608 rows, 12 tile
@@ -1401,6 +1489,12 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
       if (wma == 8) launch_big<8>(f32, gelu, nb, s, g);
       else if (wma == 7) launch_big<7>(f32, gelu, nb, s, g);
       else launch_big<6>(f32, gelu, nb, s, g);
+    } else if (use_three_slots(big * 4, K)) {
+      const dim3 grid(big * 4);
+      if (f32 && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, true, true, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
+      else if (f32) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, true, false, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
+      else if (gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, true, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
     } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
     }
