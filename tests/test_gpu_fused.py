@@ -54,6 +54,9 @@ def _random_cases(n, seed):
 
 
 CASES += _random_cases(4, 2027)
+# more than two 128 x 128 tiles per CU with K a multiple of 1536: the three-slot
+# ring (next-layer ranks 32 and 0), and the four-slot ring for a next-layer rank of 64
+CASES += [(1100, 1536, 8192, 16, 512, 32, 7), (2100, 3072, 4096, 32, 256, 0, 8), (1100, 1536, 8192, 16, 512, 64, 9)]
 
 
 @pytest.fixture(scope="module")

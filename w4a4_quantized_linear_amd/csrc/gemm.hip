@@ -538,8 +538,9 @@ __device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM, int NS = 4>
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxfp4_kernel(GemmArgs g) {
   // NS = 3: a three-slot ring (48 KiB) so that three workgroups share a CU;
-  // each step reads its own fragments at its start (plain 128 x 128 tiles).
-  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT < 0 && !QKV), "three-slot ring: plain 128 x 128 tiles");
+  // each step reads its own fragments at its start (128 x 128 tiles; the fused
+  // output quantization up to a next-layer rank of 32).
+  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT <= 2 && !QKV), "three-slot ring: 128 x 128 tiles");
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
@@ -728,8 +729,8 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
   // buffer resource of zero bytes (they write zeros into slots already consumed
   // and read no memory), and the last scale load repeats the last
   // superfragment, so that the wait counts hold throughout.  The loop is
-  // followed by a wait for every load, so that those zeros have landed before
-  // the epilogue writes its LDS staging.
+  // followed by a wait for every load of every wave (a barrier), so that those
+  // zeros have landed before the epilogue writes its LDS staging.
 #define SVDQ_FP4_STEP3(U, SCALES, VM)                                                                 \
   {                                                                                                   \
     const int step = t0 + (U);                                                                        \
@@ -769,7 +770,10 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
       SVDQ_FP4_STEP3(10, false, F + S)
       SVDQ_FP4_STEP3(11, false, F)
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): the last block's re-fetch has landed
+    // every wave's loads have landed (the zeros included: another wave's
+    // fragments share the slots this wave stages its output in) before any
+    // wave writes the ring again
+    wait_barrier<0>();
   } else {
     int sup = 0;
     for (; sup + 1 < KSUP; ++sup) {
@@ -1572,8 +1576,13 @@ hipError_t launch_gemm_quant(int fmt, const uint8_t* wblob, const WeightLayout& 
   const unsigned nb = bigt ? big : big * 4;
   const int tile_cols = bigt ? 256 : 128;
   const bool gelu = (epi & SVDQ_EPI_GELU) != 0;
+  // three 128 x 128 workgroups per CU as for the plain GEMM, up to a next-layer
+  // rank of 32 (a rank of 64 leaves too few registers)
+  const bool three = !int4 && !bigt && nwl.r_pad <= 32 && use_three_slots(nb, K);
 #define SVDQ_QLAUNCH(R16)                                                                                        \
-  if (int4 && gelu) hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, true, false, R16>), dim3(nb), dim3(256), 0, s, g); \
+  if (three && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, true, (R16 <= 2 ? R16 : 0), false, 4, 3>), dim3(nb), dim3(256), 0, s, g); \
+  else if (three) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, (R16 <= 2 ? R16 : 0), false, 4, 3>), dim3(nb), dim3(256), 0, s, g); \
+  else if (int4 && gelu) hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, true, false, R16>), dim3(nb), dim3(256), 0, s, g); \
   else if (int4) hipLaunchKernelGGL((gemm_int4_kernel<4, 4, false, false, false, R16>), dim3(nb), dim3(256), 0, s, g); \
   else if (bigt && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, true, R16>), dim3(nb), dim3(256), 0, s, g); \
   else if (bigt) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, R16>), dim3(nb), dim3(256), 0, s, g);  \
