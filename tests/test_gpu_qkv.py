@@ -57,6 +57,8 @@ def _random_cases(n, seed):
 # tiles (192 of them, a head per wave) in the fourth; then seeded random shapes
 QKV_CASES = [(300, 1024, 768, 16, 1), (17, 512, 1536, 32, 2), (256, 512, 384, 0, 3),
              (2048, 512, 6144, 16, 4)] + _random_cases(4, 2028)
+# MXFP4 only: 612 tiles of 128 x 128 with K = 1536, three workgroups per CU
+QKV_CASES += [(2100, 1536, 4608, 32, 5)]
 
 
 # every format: MXFP4 on all cases; INT4 and NVFP4 (their GEMMs take 128 x 128

@@ -539,8 +539,8 @@ template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = fal
 __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxfp4_kernel(GemmArgs g) {
   // NS = 3: a three-slot ring (48 KiB) so that three workgroups share a CU;
   // each step reads its own fragments at its start (128 x 128 tiles; the fused
-  // output quantization up to a next-layer rank of 32).
-  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT <= 2 && !QKV), "three-slot ring: 128 x 128 tiles");
+  // output quantization up to a next-layer rank of 32, the fused QKV epilogue).
+  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT <= 2), "three-slot ring: 128 x 128 tiles");
   static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
@@ -824,7 +824,9 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
     if (!LR_FIRST) add_lowrank<WN, WM>(g, acc, n0, m0, lane);
     float bv[WN][4];
     load_bias<WN>(g, n0, lane, bv);
-    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w, reinterpret_cast<uint8_t*>(slot(w)));
+    store_qkv<WN, WM>(g, acc, bv, n0, m0, lane, w,
+                      NS == 3 ? reinterpret_cast<uint8_t*>(slot(w >> 1)) + (w & 1) * 32 * stage_row_bytes<WN>()
+                              : reinterpret_cast<uint8_t*>(slot(w)));
   } else {
     // bf16 staging: 32 rows of stage_row_bytes per wave; two waves per slot with three slots
     uint8_t* const stage = NS == 3 ? reinterpret_cast<uint8_t*>(slot(w >> 1)) + (w & 1) * 32 * stage_row_bytes<WN>()
@@ -1542,6 +1544,8 @@ hipError_t launch_gemm_qkv(int fmt, const uint8_t* wblob, const WeightLayout& wl
     hipLaunchKernelGGL((gemm_nvfp4_kernel<4, 4, false, false, true>), dim3(big * 4), dim3(256), 0, s, g);
   else if (use_big_tiles(big))
     hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 8, false, false, -1, true>), dim3(big), dim3(256), 0, s, g);
+  else if (use_three_slots(big * 4, K))
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, -1, true, 4, 3>), dim3(big * 4), dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, false, false, -1, true>), dim3(big * 4), dim3(256), 0, s, g);
   return hipGetLastError();
