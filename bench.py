@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--operands", default="calibrated", choices=["calibrated", "drawn"],
                    help="layer operands: converted from the dense draw (default) or drawn look-alikes")
     p.add_argument("--no-cold", action="store_true", help="skip the cold (operand-rotating) timing")
+    p.add_argument("--no-ablation", action="store_true",
+                   help="qkv: skip the fused / unfused low-rank branch timing")
     p.add_argument("--roofline-every", type=int, default=5, metavar="N",
                    help="events around the roofline GEMM in every N-th timed step (default 5)")
     p.add_argument("--settle-ms", type=float, default=300.0,
@@ -467,9 +469,80 @@ def gpu_leg(args, ops):
     elif args.workload == "qkv":
         fused = fused_qkv(args, sq, synth, torch, np, layers[0], weights[0], inputs[0], ws[0], outs[0], epis[0], M,
                           flops[0])
+    ablation = None
+    if args.workload == "qkv" and not args.no_ablation:
+        ablation = lowrank_ablation(sq, torch, np, ops[0], layers[0], weights[0], inputs[0], ws[0], outs[0],
+                                    epis[0], M)
     return dict(value=value, ms_per_step=ms_per_step, gpu_ms_per_step=gpu_ms / args.steps, roofline=roofline,
                 breakdown=breakdown, specs=specs, fmt=specs[0].fmt, fused=fused, repeats=repeat_info, cold=cold,
-                settle_steps=settle_steps)
+                settle_steps=settle_steps, ablation=ablation)
+
+
+def lowrank_ablation(sq, torch, np, L, layer, w, x, ws, out, epi, M):
+    """What the low-rank branch costs fused, as the layer runs (the down
+    projection inside the activation quantize, the up projection in the GEMM's
+    accumulators), against run as separate kernels after the 4-bit branch: the
+    comparison of the SVDQuant notes page, section 4.3 (Fig. 6(a)), on the QKV
+    projection.  Three timings of the same layer: the 4-bit branch alone (a
+    rank-0 pack of the same residual: no D, no low-rank MFMAs); that branch
+    followed by a bf16 down projection D = X (Lambda^-1 L1) and an up projection
+    Y += D L2 as library GEMMs (torch.matmul and addmm_), which read X again and
+    Y twice; and the fused layer.  A timing ablation: the library never runs the
+    unfused branch."""
+    dev = x.device
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+    layer0 = sq.Layer(layer.fmt, layer.K, layer.N, 0)
+    w0 = sq.pack_weight(layer0, t(L["R"]), None, None, t(L["lam"]), t(L["b"]))
+    ws0 = torch.empty(sq.act_bytes(layer0, M), dtype=torch.uint8, device=dev)
+    l1 = torch.from_numpy((L["L1"].astype(np.uint32) << 16).view(np.float32)).to(dev)
+    l1s = (l1 / t(L["lam"])[:, None]).to(torch.bfloat16).contiguous()      # Lambda^-1 L1, K x r
+    l2 = t(L["L2"]).view(torch.bfloat16).contiguous()                        # r x N
+    xb = x.view(torch.bfloat16)
+    d = torch.empty((M, layer.rank), dtype=torch.bfloat16, device=dev)
+    y0 = torch.empty_like(out)
+    epi0 = epi & ~sq.EPI_LOWRANK
+
+    def fourbit():
+        sq.quantize_act(layer0, w0, x, out=ws0)
+        sq.gemm(layer0, w0, ws0, M, epi0, out=y0)
+
+    def unfused():
+        fourbit()
+        torch.matmul(xb, l1s, out=d)
+        y0.addmm_(d, l2)
+
+    def fused():
+        sq.quantize_act(layer, w, x, out=ws)
+        sq.gemm(layer, w, ws, M, epi, out=out)
+
+    variants = {"fourbit": fourbit, "unfused": unfused, "fused": fused}
+    for f in variants.values():
+        for _ in range(10):
+            f()
+    torch.cuda.synchronize()
+    res = {k: [] for k in variants}
+    for _ in range(3):
+        for k, f in variants.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            res[k].append(a.elapsed_time(b) * 1e3 / 20)
+    us = {k: sorted(v)[1] for k, v in res.items()}
+    unfused()
+    fused()
+    torch.cuda.synchronize()
+    yf, yu = out.float(), y0.float()
+    rel = float((yu - yf).abs().max() / yf.pow(2).mean().sqrt())
+    return {"fourbit_us": round(us["fourbit"], 2), "unfused_us": round(us["unfused"], 2),
+            "fused_us": round(us["fused"], 2),
+            "unfused_lowrank_overhead": round(us["unfused"] / us["fourbit"] - 1.0, 3),
+            "fused_lowrank_overhead": round(us["fused"] / us["fourbit"] - 1.0, 3),
+            "max_diff_unfused_vs_fused_over_rms": round(rel, 4),
+            "unfused_branch": "bf16 down projection X (Lambda^-1 L1) and up projection Y += D L2 as torch "
+                              "matmul / addmm_ after the rank-0 4-bit layer; medians of 3 x 20 launches each"}
 
 
 def cold_pair(args, torch, step, layers, weights, x0, ws, outs, flops, gemm_us_hot, i_dom):
@@ -774,6 +847,8 @@ def main():
         line["gpu_ms_per_step"] = round(r["gpu_ms_per_step"], 4)
     if r["fused"] is not None:
         line["fused_mlp" if len(specs) == 2 else "fused_qkv"] = r["fused"]
+    if r.get("ablation") is not None:
+        line["lowrank_ablation"] = r["ablation"]
     if r.get("repeats") is not None:
         line["repeats"] = r["repeats"]
     if r.get("cold") is not None:
