@@ -19,7 +19,10 @@ launch over its event-timed duration.
 For the MXFP4 and INT4 pairs, `fused_mlp` times the same pair with fc1's GEMM quantizing
 its output for fc2 in its epilogue (svdq_gemm_quant: three calls instead of four), same
 inputs and step count, with no event inside its timed steps either (its per-launch
-times come from a second pass); `fused_qkv` likewise for svdq_gemm_qkv.
+times come from a second pass); `fused_qkv` likewise for svdq_gemm_qkv.  With
+--workload qkv, `lowrank_ablation` times the layer's 4-bit branch alone, that
+branch with the low-rank branch as separate bf16 library GEMMs, and the fused
+layer (the comparison of the SVDQuant notes page, section 4.3, Fig. 6(a)).
 
 Operands (--operands): "calibrated" (default) converts each workload's dense
 seeded draw the way the SVDQuant notes page, section 4.2, makes a layer
