@@ -938,15 +938,23 @@ __global__ void __launch_bounds__(256, 2) gemm_int4_kernel(GemmArgs g) {
         sw0[e] = h2f(swv[e]);
         sw1[e] = h2f(swv[e] >> 16);
       }
+      // The MFMAs of block j + 1 are issued before the rescale of block j reads
+      // its sums, so the VALU does not stall on a result just issued.
+      v4i p0 = mfma_i8(a0, b0[0]), p1 = mfma_i8(a1, b1[0]);
 #pragma unroll
       for (int j = 0; j < WM; ++j) {
-        const v4i p0 = mfma_i8(a0, b0[j]);
-        const v4i p1 = mfma_i8(a1, b1[j]);
+        v4i q0 = p0, q1 = p1;
+        if (j + 1 < WM) {
+          q0 = mfma_i8(a0, b0[j + 1]);
+          q1 = mfma_i8(a1, b1[j + 1]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc[i][j][e] = fmaf(float(p0[e]), sw0[e] * sx0[j], acc[i][j][e]);
           acc[i][j][e] = fmaf(float(p1[e]), sw1[e] * sx1[j], acc[i][j][e]);
         }
+        p0 = q0;
+        p1 = q1;
       }
     }
   };
