@@ -1451,6 +1451,9 @@ static int short_tile_blocks(int64_t tiles_n, int64_t M_pad) {
 }
 
 // The 256-wide kernel with WMA activation blocks per wave.
+// INT4 / NVFP4 grids with fewer 128 x 128 tiles than this (the CU count) take 64 x 64 tiles.
+constexpr unsigned kSmallGridTiles = 256;
+
 template <int WMA>
 static void launch_big(bool f32, bool gelu, unsigned nb, hipStream_t s, const GemmArgs& g) {
   if (f32 && gelu)
@@ -1512,12 +1515,21 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
     } else {
       SVDQ_LAUNCH(gemm_mxfp4_kernel, 4, 4, 256, big * 4);
     }
-  } else if (fmt == kFmtNVFP4) {
-    const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
-    SVDQ_LAUNCH(gemm_nvfp4_kernel, 4, 4, 256, nb);
   } else {
+    // INT4 and NVFP4 are bound by the VALU work of each wave (the per-group
+    // rescale, the dequantization), which grows with the wave tile.  A grid of
+    // fewer 128 x 128 tiles than CUs takes 64 x 64 tiles instead (2 x 2 blocks
+    // per wave): four times the workgroups, a quarter of the work per wave and
+    // step, and for every output the same operations in the same order.
     const unsigned nb = unsigned((wl.N_pad / 128) * (al.M_pad / 128));
-    SVDQ_LAUNCH(gemm_int4_kernel, 4, 4, 256, nb);
+    if (nb < kSmallGridTiles) {
+      if (fmt == kFmtNVFP4) SVDQ_LAUNCH(gemm_nvfp4_kernel, 2, 2, 256, nb * 4);
+      else SVDQ_LAUNCH(gemm_int4_kernel, 2, 2, 256, nb * 4);
+    } else if (fmt == kFmtNVFP4) {
+      SVDQ_LAUNCH(gemm_nvfp4_kernel, 4, 4, 256, nb);
+    } else {
+      SVDQ_LAUNCH(gemm_int4_kernel, 4, 4, 256, nb);
+    }
   }
 #undef SVDQ_LAUNCH
   return hipGetLastError();
