@@ -154,6 +154,37 @@ def test_tile_schedules_elementwise(torch_dev):
         check_fp32_output(Y.cpu().numpy(), ref["Y"], f"M={M} N={N}")
 
 
+@pytest.mark.parametrize("fmt", ["int4", "nvfp4"])
+def test_int4_nvfp4_tile_sizes(torch_dev, fmt):
+    """INT4 and NVFP4 layers with fewer 128 x 128 output tiles than CUs take
+    64 x 64 tiles.  2048 x 1024 -> 4352 (544 tiles of 128 x 128) against the
+    oracle element by element, with and without the low-rank branch; at rank 0
+    the rows are independent, so its first 200 rows computed as a 200-row layer
+    (68 tiles of 128 x 128: the 64 x 64 schedule) must give the same bits, in
+    fp32 and in bf16 with GELU."""
+    torch, dev = torch_dev
+    M, K, N = 2048, 1024, 4352
+    for rank in (0, 32):
+        spec, L = _medium_layer("qkv", fmt, M, K, N, rank, 60 + rank)
+        layer = sq.Layer(fmt, K, N, rank)
+        print(f"{fmt} tile sizes rank {rank}", flush=True)
+        w = pack(layer, L, torch, dev)
+        X = dev_tensor(L["X"], torch, dev)
+        epi = sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_OUT_F32
+        Yf = sq.linear(layer, w, X, epi)
+        Yg = sq.linear(layer, w, X, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU)
+        torch.cuda.synchronize()
+        ref = Ly.forward(L["X"], L["lam"], L["L1"], L["L2"], L["R"], L["b"], fmt)
+        check_fp32_output(Yf.cpu().numpy(), ref["Y"], f"{fmt} M={M} rank {rank}")
+        if rank == 0:
+            Xs = dev_tensor(L["X"][:200], torch, dev)
+            Ysf = sq.linear(layer, w, Xs, epi)
+            Ysg = sq.linear(layer, w, Xs, sq.EPI_LOWRANK | sq.EPI_BIAS | sq.EPI_GELU)
+            torch.cuda.synchronize()
+            assert torch.equal(Ysf.view(torch.int32), Yf[:200].view(torch.int32)), "fp32 rows differ by tile size"
+            assert torch.equal(Ysg.view(torch.int16), Yg[:200].view(torch.int16)), "bf16 GELU rows differ by tile size"
+
+
 def test_short_tiles_elementwise(torch_dev):
     """256-wide tiles shorter than 256 rows, chosen when they fill more CUs in
     one round: 4600 x 3072 (12 tile columns: 252 tiles of 224 rows, the last
