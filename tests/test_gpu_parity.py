@@ -240,11 +240,12 @@ def test_one_tile_per_cu_elementwise(torch_dev, M, K, N, rank, seed):
                          ids=["544-tiles-K1536-r48", "585-tiles-K3072"])
 def test_three_per_cu_elementwise(torch_dev, M, K, N, rank, seed):
     """MXFP4 grids of more than two 128 x 128 tiles per CU with K a multiple of
-    1536 take the three-slot ring (three workgroups per CU, blocks of twelve
-    128-K steps whose last two loads read nothing): one and two blocks, ragged M
-    and N.  fp32, bf16, bias-free bf16 and GELU outputs element by element
-    against the oracle; bf16 must be the round-to-nearest-even of fp32 (the
-    bf16 stores are staged through the ring after the loop)."""
+    1536 take a three-slot ring (blocks of twelve 128-K steps whose last two
+    loads read nothing): 256 x 128 tiles at two workgroups per CU without GELU
+    (the fp32, bf16 and bias-free outputs), 128 x 128 tiles at three per CU with
+    it (the GELU output); one and two blocks, ragged M and N.  Every output
+    element by element against the oracle; bf16 must be the round-to-nearest-even
+    of fp32 (the bf16 stores are staged through the ring after the loop)."""
     torch, dev = torch_dev
     spec, L = _medium_layer("qkv", "mxfp4", M, K, N, rank, seed)
     layer = sq.Layer("mxfp4", K, N, rank)

@@ -536,19 +536,26 @@ __device__ __forceinline__ void raster_tile(int t, int tiles_m, int tiles_n, int
 }
 
 template <int WN, int WM, bool OUT_F32, bool GELU, int QOUT = -1, bool QKV = false, int WMA = WM, int NS = 4>
-__global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxfp4_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256, WN == 8 ? (NS == 3 ? 2 : 1) : (NS == 3 ? 3 : 2)) gemm_mxfp4_kernel(GemmArgs g) {
   // NS = 3: a three-slot ring (48 KiB) so that three workgroups share a CU;
   // each step reads its own fragments at its start (128 x 128 tiles; the fused
   // output quantization up to a next-layer rank of 32, the fused QKV epilogue).
-  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT <= 2), "three-slot ring: 128 x 128 tiles");
-  static_assert(WN == WM && (WN == 8 || WN == 4), "square wave tiles of 8 x 8 or 4 x 4 blocks");
+  // 256 x 128 tiles (8 x 4 blocks per wave) take a three-slot ring of 72 KiB,
+  // two workgroups per CU.
+  constexpr bool RECT = WN == 8 && WM == 4;
+  static_assert(NS == 4 || (NS == 3 && WN == 4 && QOUT <= 2) || (NS == 3 && RECT && QOUT < 0 && !QKV),
+                "three-slot ring: 128 x 128 or 256 x 128 tiles");
+  static_assert((WN == WM && (WN == 8 || WN == 4)) || (RECT && NS == 3), "wave tiles of 8 x 8, 4 x 4 or 8 x 4 blocks");
   static_assert(!QKV || (QOUT < 0 && !OUT_F32 && !GELU), "the QKV epilogue stores bf16 with no activation");
   // Short tiles: WMA < WM active activation blocks per wave, a 256 x 32 WMA tile.
   static_assert(WMA == WM || (WN == 8 && QOUT < 0 && !QKV && WMA > WM / 2 && WMA < WM), "short tiles");
-  constexpr int SF = 2 * WN;            // fragments per operand per stage
-  constexpr int PW = SF / 4;            // fragments per operand that each wave fetches
-  constexpr int SU4 = 2 * SF * 64;      // uint4 per stage (weights, then activations)
-  static_assert(2 * PW == WN, "each wave row issues one fragment load per step");
+  constexpr int SF = 2 * WN;            // weight fragments per stage
+  constexpr int SFB = 2 * WM;           // activation fragments per stage
+  constexpr int PW = SF / 4;            // weight fragments that each wave fetches per stage
+  constexpr int PWB = SFB / 4;          // activation fragments that each wave fetches per stage
+  constexpr int FW = PW + PWB;          // fragment loads per wave and stage
+  constexpr int SU4 = (SF + SFB) * 64;  // uint4 per stage (weights, then activations)
+  static_assert(FW <= WN, "each wave row issues at most one fragment load per step");
   __shared__ uint4 ring0[SU4], ring1[SU4], ring2[SU4], ring3[NS == 4 ? SU4 : 1];   // 4 x 32 KiB (8 x 8) or 4 x 16 KiB
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -576,7 +583,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
   // A stage always holds SF activation fragments; with short tiles the last
   // 2 (WM - WMA) are not read, and the view stops at the padded rows (loads
   // past it return zeros; those rows are never stored).
-  const int64_t act_rt = g.M_pad / 16 - mt0 < SF ? g.M_pad / 16 - mt0 : SF;
+  const int64_t act_rt = g.M_pad / 16 - mt0 < SFB ? g.M_pad / 16 - mt0 : SFB;
   const uint32_t code_bytes = uint32_t(SF) * KS * 1024, scale_bytes = uint32_t(SF) * KSUP * 256;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.wblob + g.w_codes + size_t(nt0) * KS * 1024, code_bytes);
   const __amdgpu_buffer_rsrc_t rB =
@@ -601,8 +608,9 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
   auto fetch1 = [&](uint4* dst_stage, int step, int f) {
     const bool wt = f < PW;
     const int fi = wt ? f : f - PW;
-    const uint32_t so = uint32_t((PW * w + fi) * KS + step) * 1024;
-    load_frag_lds(wt ? rA : rB, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
+    const int fr = (wt ? PW : PWB) * w + fi;     // the fragment's row tile in its operand
+    const uint32_t so = uint32_t(fr * KS + step) * 1024;
+    load_frag_lds(wt ? rA : rB, dst_stage + ((wt ? 0 : SF) + fr) * 64, voff16, so);
   };
   // The same, or (!valid) the same load through a buffer resource of zero
   // bytes: every lane is out of range, so it writes zeros and reads no memory.
@@ -610,8 +618,9 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
   auto fetch1x = [&](uint4* dst_stage, int step, int f, bool valid) {
     const bool wt = f < PW;
     const int fi = wt ? f : f - PW;
-    const uint32_t so = uint32_t((PW * w + fi) * KS + step) * 1024;
-    load_frag_lds(valid ? (wt ? rA : rB) : rZ, dst_stage + ((wt ? 0 : SF) + PW * w + fi) * 64, voff16, so);
+    const int fr = (wt ? PW : PWB) * w + fi;
+    const uint32_t so = uint32_t(fr * KS + step) * 1024;
+    load_frag_lds(valid ? (wt ? rA : rB) : rZ, dst_stage + ((wt ? 0 : SF) + fr) * 64, voff16, so);
   };
   auto frag_a = [&](const uint4* st, int i) { return st[(wn * WN + i) * 64 + lane]; };
   auto frag_b = [&](const uint4* st, int j) { return st[(SF + wm * WMA + j) * 64 + lane]; };
@@ -622,7 +631,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
   // stages 0..2 (into slots 0..2), and its MFMAs run while those land; further
   // 32-rank chunks follow in order.  256-wide tiles (no registers to spare
   // here) add the low-rank term after the main loop instead.
-  constexpr bool LR_FIRST = WN == 4;
+  constexpr bool LR_FIRST = WN == 4 || RECT;
   v4f acc[WN][WMA];
 #pragma unroll
   for (int i = 0; i < WN; ++i)
@@ -655,12 +664,12 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
     if (lowrank) lowrank_operands(0, l2, dh, dl);
     load_scales(sa, sb, 0);
 #pragma unroll
-    for (int f = 0; f < 2 * PW; ++f) fetch1(ring0, 0, f);
+    for (int f = 0; f < FW; ++f) fetch1(ring0, 0, f);
 #pragma unroll
-    for (int f = 0; f < 2 * PW; ++f) fetch1(ring1, 1, f);
+    for (int f = 0; f < FW; ++f) fetch1(ring1, 1, f);
     if constexpr (NS == 4) {
 #pragma unroll
-      for (int f = 0; f < 2 * PW; ++f) fetch1(ring2, 2, f);
+      for (int f = 0; f < FW; ++f) fetch1(ring2, 2, f);
     }
     if (lowrank) {
       lowrank_mfma(l2, dh, dl);
@@ -670,7 +679,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
       }
     }
   }
-  wait_barrier<2 * PW>();                          // stages 0 and 1 (three slots: stage 0) are in LDS
+  wait_barrier<FW>();                              // stages 0 and 1 (three slots: stage 0) are in LDS
   // Fragments in registers, reloaded in place.  A step runs its 8 x 8 MFMAs in
   // two halves by activation fragment: half 0 uses fb[0..3] and meanwhile reads
   // fb[4..7] of the same stage; half 1 uses fb[4..7] and meanwhile reads the
@@ -741,7 +750,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
     _Pragma("unroll") for (int j = 0; j < WM; ++j) fb[j] = frag_b(sc, j);                             \
     _Pragma("unroll") for (int i = 0; i < WN; ++i) fa[i] = frag_a(sc, i);                             \
     _Pragma("unroll") for (int i = 0; i < WN; ++i) {                                                  \
-      fetch1x(sf, step + 2, i, fv);                                                                   \
+      if (i < FW) fetch1x(sf, step + 2, i, fv);                                                       \
       _Pragma("unroll") for (int j = 0; j < WM; ++j)                                                  \
         acc[i][j] = mfma_fp4_sel<((U) & 3)>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);                   \
       __builtin_amdgcn_sched_barrier(0);                                                              \
@@ -755,7 +764,7 @@ __global__ void __launch_bounds__(256, WN == 8 ? 1 : (NS == 3 ? 3 : 2)) gemm_mxf
     }                                                                                                 \
   }
   if constexpr (NS == 3) {
-    constexpr int F = 2 * PW, S = WN + WMA;        // loads per stage, per superfragment's scales
+    constexpr int F = FW, S = WN + WMA;            // loads per stage, per superfragment's scales
     for (int t0 = 0; t0 < KS; t0 += 12) {
       SVDQ_FP4_STEP3(0, false, F)
       SVDQ_FP4_STEP3(1, true, F + S)
@@ -1506,6 +1515,16 @@ hipError_t launch_gemm(int fmt, const uint8_t* wblob, const WeightLayout& wl, co
       if (wma == 8) launch_big<8>(f32, gelu, nb, s, g);
       else if (wma == 7) launch_big<7>(f32, gelu, nb, s, g);
       else launch_big<6>(f32, gelu, nb, s, g);
+    } else if (!gelu && use_three_slots(big * 4, K)) {
+      // 256 x 128 tiles, 8 x 4 blocks per wave and two workgroups per CU on a
+      // 72 KiB three-slot ring: 12 fragment reads per 32 MFMAs instead of 8 per
+      // 16, and the same operations per output as the 128 x 128 tiles (the
+      // same bits).  Without GELU only: with it, the 128 x 128 tiles at three
+      // per CU hide more of the VALU-heavy epilogue (measured level at FLUX fc1;
+      // the LoRA layer 103.5 -> 97.6 us).
+      const dim3 grid(big * 2);
+      if (f32) hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 4, true, false, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((gemm_mxfp4_kernel<8, 4, false, false, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
     } else if (use_three_slots(big * 4, K)) {
       const dim3 grid(big * 4);
       if (f32 && gelu) hipLaunchKernelGGL((gemm_mxfp4_kernel<4, 4, true, true, -1, false, 4, 3>), grid, dim3(256), 0, s, g);
