@@ -496,7 +496,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, v4f (&acc)[WN][WM], 
 // superfragment ahead; the MFMA of step u of the superfragment picks byte u.
 // The 128 x 128 tiles also come with a three-slot ring (NS = 3, 48 KiB, three
 // workgroups per CU): there step t reads its own fragments first and loads
-// stage t+2 into the slot of stage t-1.
+// stage t+2 into the slot of stage t-1.  The same ring serves 256 (n) x 128 (m)
+// tiles of 8 x 4 blocks per wave (a stage of 16 weight and 8 activation
+// fragments, 72 KiB, two workgroups per CU).
 
 
 __device__ __forceinline__ uint4 load_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
